@@ -1,0 +1,135 @@
+"""Plain fp64 paged FP8-KV attention -- TEST INFRASTRUCTURE ONLY.
+
+The definition followed:
+  * Atlas engine article (ainews.cool), "技术深度解析":
+      - memory section: the KV cache lives in fixed-size blocks taken from a
+        preallocated pool; a sequence's blocks are found through its block
+        table (the paged KV cache of the GB10 article);
+      - quantisation section: FP8 storage with per-group scale factors; here
+        one fp32 scale per (page, kv head), separate for K and V, and
+        value = decoded byte * scale;
+      - attention section: a FlashAttention-2 variant with native MQA/GQA.
+        FA2's online softmax computes exactly softmax(Q K^T / sqrt(d)) V, so
+        the oracle is that formula, evaluated directly in fp64.
+  * GB10 article (ainews.surl.tw): MTP with K=4 draft tokens -> a sequence
+    may bring several new query tokens; they attend causally (token i of
+    Q new tokens sees keys 0 .. L-Q+i, where L counts every key including
+    the new ones).
+
+Readings where the pages are silent (each listed in the design notes):
+  * GQA grouping: query head hq uses kv head hq // (Hq / Hkv).
+  * Layouts: k_pages [P][Hkv][S][D]; v_pages [P][Hkv][S/4][D][4], i.e. the
+    byte of token slot s at dim d of a (page, head) sits at
+    ((s // 4) * D + d) * 4 + s % 4.
+  * Scale 1/sqrt(D) unless given; no soft-cap, ALiBi, window or sinks.
+  * Bytes past a sequence's length and unreferenced pages are never read.
+
+The small helpers below name each reading separately, so the tests can
+replace one of them with a plausible mistake and check that a pin fails.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import e4m3
+
+
+def kv_head_of(hq: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """GQA/MQA: consecutive groups of Hq/Hkv query heads share one kv head."""
+    return hq // (num_q_heads // num_kv_heads)
+
+
+def last_visible_key(ctx_len: int, q_len: int, i: int) -> int:
+    """Causal limit of new token i: keys 0..L-Q+i (bottom-right alignment)."""
+    return ctx_len - q_len + i
+
+
+def token_location(block_table_row: np.ndarray, t: np.ndarray, page_size: int):
+    """Logical token t -> (physical page, slot inside the page)."""
+    return block_table_row[t // page_size], t % page_size
+
+
+def k_token_bytes(k_pages: np.ndarray, pages: np.ndarray, h: int, slots: np.ndarray) -> np.ndarray:
+    """K bytes of (page, head h, slot) for each token: [T][D]."""
+    return k_pages[pages, h, slots, :]
+
+
+def v_token_bytes(v_pages: np.ndarray, pages: np.ndarray, h: int, slots: np.ndarray) -> np.ndarray:
+    """V bytes of (page, head h, slot) for each token: [T][D] (4-token interleave)."""
+    return v_pages[pages, h, slots // 4, :, slots % 4]
+
+
+def softmax_scale(head_dim: int, sm_scale: float | None) -> float:
+    return 1.0 / np.sqrt(head_dim) if not sm_scale else float(sm_scale)
+
+
+@dataclass
+class GatheredSequence:
+    k_bytes: np.ndarray  # uint8 [Hkv][L][D]
+    v_bytes: np.ndarray  # uint8 [Hkv][L][D]
+    k_scale: np.ndarray  # float64 [Hkv][L]
+    v_scale: np.ndarray  # float64 [Hkv][L]
+    page_of_token: np.ndarray  # int64 [L]
+
+
+def gather_sequence(k_pages, v_pages, kv_scales, block_table_row, ctx_len: int) -> GatheredSequence:
+    """Follow one sequence's block table and collect its L tokens' bytes and scales."""
+    k_pages = np.asarray(k_pages)
+    v_pages = np.asarray(v_pages)
+    _, hkv, page_size, d = k_pages.shape
+    t = np.arange(int(ctx_len))
+    pages, slots = token_location(np.asarray(block_table_row).astype(np.int64), t, page_size)
+    kb = np.empty((hkv, t.size, d), dtype=np.uint8)
+    vb = np.empty((hkv, t.size, d), dtype=np.uint8)
+    ks = np.empty((hkv, t.size), dtype=np.float64)
+    vs = np.empty((hkv, t.size), dtype=np.float64)
+    for h in range(hkv):
+        kb[h] = k_token_bytes(k_pages, pages, h, slots)
+        vb[h] = v_token_bytes(v_pages, pages, h, slots)
+        ks[h] = kv_scales[0][pages, h]
+        vs[h] = kv_scales[1][pages, h]
+    return GatheredSequence(kb, vb, ks, vs, pages)
+
+
+def paged_attention(q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, *,
+                    num_kv_heads: int, sm_scale: float | None = None, rows=None) -> np.ndarray:
+    """out[r][hq][:] = sum_t softmax_t(z) * V~[t], z_t = scale * <q[r][hq], K~[t]>.
+
+    q: [sum Q][Hq][D] (any real dtype; read exactly into fp64).
+    rows: optional iterable of global query rows to evaluate (others stay 0).
+    Returns fp64 [sum Q][Hq][D].
+    """
+    if hasattr(q, "detach"):  # torch tensor
+        q = q.detach().to("cpu").double().numpy()
+    q = np.asarray(q, dtype=np.float64)
+    total_q, num_q_heads, d = q.shape
+    ctx_lens = np.asarray(ctx_lens).astype(np.int64)
+    q_lens = np.asarray(q_lens).astype(np.int64)
+    scale = softmax_scale(d, sm_scale)
+    want = None if rows is None else set(int(r) for r in rows)
+    out = np.zeros((total_q, num_q_heads, d), dtype=np.float64)
+
+    row0 = 0
+    for b in range(len(q_lens)):
+        L, Q = int(ctx_lens[b]), int(q_lens[b])
+        mine = [i for i in range(Q) if want is None or (row0 + i) in want]
+        if mine:
+            g = gather_sequence(k_pages, v_pages, kv_scales, block_table[b], L)
+            k_deq = [e4m3.decode(g.k_bytes[h]) * g.k_scale[h][:, None] for h in range(num_kv_heads)]
+            v_deq = [e4m3.decode(g.v_bytes[h]) * g.v_scale[h][:, None] for h in range(num_kv_heads)]
+            idx = np.array(mine)
+            lim = np.array([last_visible_key(L, Q, i) for i in mine])  # [n]
+            visible = np.arange(L)[None, :] <= lim[:, None]  # [n][L]
+            for hq in range(num_q_heads):
+                h = kv_head_of(hq, num_q_heads, num_kv_heads)
+                z = (q[row0 + idx, hq, :] @ k_deq[h].T) * scale  # [n][L]
+                z = np.where(visible, z, -np.inf)
+                z = z - z.max(axis=1, keepdims=True)
+                w = np.exp(z)
+                w = w / w.sum(axis=1, keepdims=True)
+                out[row0 + idx, hq, :] = w @ v_deq[h]
+        row0 += Q
+    return out

@@ -1,0 +1,10 @@
+"""Seeded synthetic inputs for paged FP8-KV attention (input generation only)."""
+
+from .workloads import (  # noqa: F401
+    CONFIGS,
+    PAGE_SIZE,
+    POISON_BYTE,
+    Workload,
+    custom_workload,
+    make_workload,
+)
