@@ -1,0 +1,305 @@
+"""Benchmark of paged FP8-KV attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one forward of the whole path (block-table gather, FP8 dequant,
+GQA QK^T, online softmax, PV, partition merge -- one kernel launch) over one
+batch of synthetic input.  Default workload: the LLaMA-3-8B-shaped decode
+batch (32 sequences, 32 query / 8 KV heads, head_dim 128, contexts uniform in
+512..4096, FP8 E4M3 KV in 16-token pages of a shuffled pool).  Inputs are
+resident in HBM before timing starts; each forward reads a different copy of
+the KV pool from a rotation set of >= 1 GiB so that neither L2 nor the
+256 MB Infinity Cache can serve the KV.  Forwards are launched as one HIP
+graph of K nodes (``--eager`` launches them one by one from Python).
+
+Prints one JSON line (rank 0): metric/value (KV-path HBM GB/s), query
+tokens/s, the roofline of the attention kernel, and the CPU oracle's rate on
+a bounded sample of the same workload (``cpu_baseline``).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import resource
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged FP8-KV GQA attention: KV HBM GB/s (% of peak), query-tokens/s at bs=32"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+ROTATION_BYTES = 1 << 30
+KERNEL_SOURCE = os.path.join(ROOT, "paged_fp8_kv_attn_amd", "csrc", "attn_stream.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_counts(w) -> dict:
+    """Bytes and flops the method itself must move/do per forward."""
+    L = w.ctx_lens.astype(np.int64)
+    Q = w.q_lens.astype(np.int64)
+    pages = (L + w.page_size - 1) // w.page_size
+    kv = int((L * w.num_kv_heads * w.head_dim * 2).sum())
+    scales = int((pages * w.num_kv_heads * 8).sum())
+    bt = int((pages * 4).sum())
+    qb = 4 if w.q_dtype == "f32" else 2
+    ob = 4 if w.out_dtype == "f32" else 2
+    q_bytes = int(Q.sum()) * w.num_q_heads * w.head_dim * qb
+    out_bytes = int(Q.sum()) * w.num_q_heads * w.head_dim * ob
+    lens = 8 * w.num_seqs
+    pairs = int(sum(int(Q[b]) * (int(L[b]) - int(Q[b])) + int(Q[b]) * (int(Q[b]) + 1) // 2 for b in range(w.num_seqs)))
+    flops = 4 * w.head_dim * w.num_q_heads * pairs
+    return dict(bytes=kv + scales + bt + q_bytes + out_bytes + lens, kv_bytes=kv, flops=flops, pairs=pairs,
+                query_tokens=int(Q.sum()))
+
+
+def workload_config(w) -> dict:
+    return {
+        "workload": w.name,
+        "batch": w.num_seqs,
+        "q_heads": w.num_q_heads,
+        "kv_heads": w.num_kv_heads,
+        "head_dim": w.head_dim,
+        "page_size": w.page_size,
+        "q_len": sorted(set(int(x) for x in w.q_lens))[:4],
+        "ctx_min": int(w.ctx_lens.min()),
+        "ctx_max": int(w.ctx_lens.max()),
+        "ctx_mean": float(w.ctx_lens.mean()),
+        "kv_format": "fp8_e4m3 (OCP), fp32 scale per (page, kv head)",
+        "q_dtype": w.q_dtype,
+        "out_dtype": w.out_dtype,
+        "seed": w.seed,
+    }
+
+
+def source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"attn_stream_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, counts, budget_s: float) -> dict:
+    """Time the oracle (as it stands) on the host over whole passes of the
+    workload's sequences until about budget_s seconds have been spent."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+        ncpu = len(os.sched_getaffinity(0))
+        limiter = threadpool_limits(limits=ncpu)
+    except Exception:  # pragma: no cover
+        ncpu, limiter = os.cpu_count() or 1, None
+    # sequences sampled in order; whole sequences, all heads
+    done_seqs = 0
+    done_bytes = 0
+    done_tokens = 0
+    per_seq_bytes = None
+    t0 = time.perf_counter()
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    row0 = np.concatenate([[0], np.cumsum(w.q_lens)]).astype(np.int64)
+    L = w.ctx_lens.astype(np.int64)
+    pages = (L + w.page_size - 1) // w.page_size
+    qb = 4 if w.q_dtype == "f32" else 2
+    ob = 4 if w.out_dtype == "f32" else 2
+    per_seq_bytes = (L * w.num_kv_heads * w.head_dim * 2 + pages * w.num_kv_heads * 8 + pages * 4
+                     + w.q_lens.astype(np.int64) * w.num_q_heads * w.head_dim * (qb + ob) + 8)
+    b = 0
+    while True:
+        rows = list(range(int(row0[b]), int(row0[b + 1])))
+        oracle.paged_attention(w.q, w.k_pages, w.v_pages, w.kv_scales, w.block_table, w.ctx_lens, w.q_lens,
+                               num_kv_heads=w.num_kv_heads, sm_scale=w.sm_scale, rows=rows)
+        done_seqs += 1
+        done_bytes += int(per_seq_bytes[b])
+        done_tokens += int(w.q_lens[b])
+        b = (b + 1) % w.num_seqs
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {
+        "value": done_bytes / wall / 1e9,
+        "unit": "GB/s",
+        "cores": max(1, int(math.ceil(cpu / wall - 0.05))),
+        "kind": "oracle",
+        "sample": (f"{done_seqs} sequence forwards (whole sequences in order, all heads) of the same workload, "
+                   f"{wall:.1f} s wall, {cpu:.1f} s CPU on {ncpu} allowed threads; fp64 numpy oracle; "
+                   f"{done_tokens / wall:.1f} query-tokens/s"),
+        "query_tokens_per_s": done_tokens / wall,
+        "threads_allowed": ncpu,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_decode")
+    ap.add_argument("--eager", action="store_true", help="launch forwards one by one instead of one HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--json-out", default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention path runs whole on a single MI355X "
+              "and this build has no multi-GPU mode (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "reps": 5}))
+        return
+
+    from paged_fp8_kv_attn_amd import Plan, load_library
+    from synth import make_workload
+
+    load_library()
+    t_gen = time.perf_counter()
+    w = make_workload(args.workload, keep_logical=False)
+    t_gen = time.perf_counter() - t_gen
+    counts = algorithmic_counts(w)
+
+    plan = Plan(num_seqs=w.num_seqs, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                num_pages=w.num_pages, max_pages_per_seq=w.max_pages_per_seq, max_q_len=w.max_q_len,
+                max_ctx_len=w.max_ctx_len, q_dtype=w.q_dtype, out_dtype=w.out_dtype, sm_scale=w.sm_scale,
+                num_kv_splits=w.num_kv_splits)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    q = w.q.to(dev)
+    bt = t(w.block_table)
+    ctx = t(w.ctx_lens)
+    ql = t(w.q_lens)
+    k0, v0, s0 = t(w.k_pages), t(w.v_pages), t(w.kv_scales)
+    pool_bytes = k0.numel() + v0.numel() + s0.numel() * 4
+    copies = max(2, math.ceil(ROTATION_BYTES / pool_bytes))
+    pools = [(k0, v0, s0)] + [(k0.clone(), v0.clone(), s0.clone()) for _ in range(copies - 1)]
+    out_dt = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
+    out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=out_dt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd(i):
+        k, v, s = pools[i % copies]
+        plan.forward(q, k, v, s, bt, ctx, ql, out, stream=stream)
+
+    for i in range(args.warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            graph.capture_begin()
+            for i in range(args.steps):
+                k, v, s = pools[i % copies]
+                plan.forward(q, k, v, s, bt, ctx, ql, out, stream=cap)
+            graph.capture_end()
+        stream.wait_stream(cap)
+        graph.replay()  # one untimed replay of the captured steps
+        torch.cuda.synchronize()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            fwd(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    ms = total_ms / args.steps
+
+    gbs = counts["bytes"] / (ms * 1e-3) / 1e9
+    tflops = counts["flops"] / (ms * 1e-3) / 1e12
+    qtok = counts["query_tokens"] / (ms * 1e-3)
+    prefill_like = counts["flops"] / max(1, counts["bytes"]) > 312  # above the bf16 ridge point
+    traffic = committed_traffic(w.name)
+    if prefill_like:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}
+    roof.update({"kernel": "attn_stream_kernel", "algorithmic_bytes_per_launch": counts["bytes"],
+                 "algorithmic_flops_per_launch": counts["flops"], "launches_per_step": 1})
+
+    res = {
+        "metric": METRIC,
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": workload_config(w),
+        "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "query_tokens_per_s": qtok,
+        "tflops": tflops,
+        "launch": "graph" if graph is not None else "eager",
+        "kv_pool_copies": copies,
+        "plan": plan.info(),
+        "kernel_source_sha256_16": source_hash(),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, counts, args.cpu_seconds)
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged FP8-KV attention library.
+ *
+ * One operation: attention of new query tokens over a KV cache that is kept
+ * in fixed-size pages of a preallocated pool, stored as FP8 E4M3 bytes with
+ * one fp32 scale per (page, kv head), with grouped/multi-query heads.
+ *
+ * The operation follows these passages:
+ *   - Atlas engine article (ainews.cool), section "技术深度解析":
+ *       memory architecture -- KV cache in fixed-size blocks preallocated from
+ *         a pool, no allocation while serving (hence the plan object, which
+ *         allocates its workspace once, and the allocation-free forward);
+ *       attention -- a FlashAttention-2 variant with tiling chosen per
+ *         sequence length and GPU, and dedicated MQA/GQA kernels;
+ *       quantisation -- FP8 with per-group scale factors fused into kernels.
+ *   - "Atlas Takes On vLLM With a Pure Rust/CUDA Inference Engine on a
+ *     Single GB10" (ainews.surl.tw): a paged FP8 KV cache; multi-token
+ *     prediction with K=4 draft tokens, whose verification is attention of
+ *     1+K causal query tokens per sequence.
+ *
+ * Result (exact arithmetic): for sequence b with L_b keys and Q_b new query
+ * tokens, new token i (0-based) and query head hq,
+ *     h      = hq / (Hq / Hkv)                       (kv head of the group)
+ *     K~[t]  = e4m3(k byte of token t, head h) * kv_scales[0][page(t)][h]
+ *     V~[t]  = e4m3(v byte of token t, head h) * kv_scales[1][page(t)][h]
+ *     z_t    = sm_scale * <q[r_b+i][hq][:], K~[t]>   for t <= L_b - Q_b + i
+ *     out[r_b+i][hq][:] = sum_t softmax(z)_t * V~[t]
+ * where r_b = Q_0 + ... + Q_{b-1} and page(t) = block_table[b][t / 16].
+ *
+ * Memory layouts (all buffers are device memory, caller-owned):
+ *   q           [sum Q_b][Hq][D]  ATTN_DTYPE_BF16 or ATTN_DTYPE_F32
+ *   k_pages     uint8 [P][Hkv][16][D]        token-major within (page, head)
+ *   v_pages     uint8 [P][Hkv][4][D][4]      inside a (page, head): the
+ *               byte of slot s, dim d sits at ((s/4)*D + d)*4 + s%4
+ *   kv_scales   fp32  [2][P][Hkv]            [0] K scales, [1] V scales
+ *   block_table int32 [B][max_pages_per_seq] physical page ids
+ *   ctx_lens    int32 [B]   L_b (counts the Q_b new tokens, whose K/V are
+ *                            already in the pages)
+ *   q_lens      int32 [B]   Q_b
+ *   out         [sum Q_b][Hq][D]  ATTN_DTYPE_BF16 (round to nearest even)
+ *               or ATTN_DTYPE_F32
+ * E4M3 is the OCP 8-bit floating point E4M3 format (bias 7, max 448, NaN
+ * only at 0x7F/0xFF).
+ *
+ * Device-data preconditions (not checked on the hot path; breaking one is
+ * undefined and may fault):
+ *   1 <= Q_b <= max_q_len, Q_b <= L_b <= max_ctx_len;
+ *   block_table[b][j] in [0, P) for j < ceil(L_b / 16);
+ *   the K/V bytes of tokens t < L_b are not NaN codes.
+ * Entries of block_table past ceil(L_b/16), bytes of slots >= L_b in the last
+ * page and every unreferenced page are never used (they may hold anything).
+ *
+ * Errors: every entry point returns an attn_status_t.  Host-checkable
+ * problems (null or misaligned pointers, bad descriptor) return before any
+ * device work is enqueued.  A failed HIP call returns ATTN_ERR_HIP; the HIP
+ * error code is then available from attn_last_hip_error() on that thread.
+ *
+ * Threading: a plan may be used by one stream at a time (its workspace is
+ * shared by the forwards it enqueues); distinct plans are independent.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct attn_plan_s* attn_plan_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, inconsistent descriptor */
+  ATTN_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+  ATTN_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed */
+  ATTN_ERR_HIP = 4               /* a HIP runtime call failed */
+} attn_status_t;
+
+typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype_t;
+
+/* Static shape of the work a plan serves (the "adaptive tiling" of the
+ * attention section: tile and split sizes are chosen from it once). */
+typedef struct {
+  int32_t num_seqs;          /* B >= 1 */
+  int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;      /* Hkv >= 1 */
+  int32_t head_dim;          /* D: 64 or 128 */
+  int32_t page_size;         /* S: 16 */
+  int32_t num_pages;         /* P: pages in the pool */
+  int32_t max_pages_per_seq; /* row stride of block_table, >= ceil(max_ctx_len/16) */
+  int32_t max_q_len;         /* bound on every Q_b, >= 1 */
+  int32_t max_ctx_len;       /* bound on every L_b, >= max_q_len */
+  attn_dtype_t q_dtype;      /* BF16 or F32 */
+  attn_dtype_t out_dtype;    /* BF16 or F32 */
+  float sm_scale;            /* softmax scale; 0 means 1/sqrt(head_dim) */
+  int32_t num_kv_splits;     /* 0: plan chooses; n >= 1: split each sequence's
+                                keys into at most n partitions merged by
+                                log-sum-exp */
+  int32_t reserved[4];       /* must be zero */
+} attn_plan_desc_t;
+
+/* What the plan chose (for tests and measurement). */
+typedef struct {
+  int32_t col_tiles;        /* 16-column MFMA tiles per workgroup (1, 2 or 4) */
+  int32_t dup_lo_columns;   /* 1: low parts of P ride in spare MFMA columns */
+  int32_t cols_per_block;   /* query columns (token x head of a group) per workgroup */
+  int32_t col_blocks;       /* workgroups along the query columns of a group */
+  int32_t waves_per_group;  /* waves per workgroup */
+  int32_t num_kv_splits;    /* partitions per (sequence, kv head, column block) */
+  int32_t tokens_per_split; /* keys per partition (multiple of 32) */
+  int32_t grid_size;        /* workgroups of the attention kernel */
+  size_t workspace_bytes;   /* device bytes owned by the plan */
+} attn_plan_info_t;
+
+/* Validate desc, choose tiles/splits, allocate the workspace once with
+ * hipMalloc on the current device.  On success *plan owns that memory.
+ * No device work is enqueued. */
+attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* plan);
+
+/* Enqueue the attention on `stream` (asynchronous: no allocation, no host
+ * synchronisation).  Pointers are device pointers in the layouts above;
+ * q, k_pages, v_pages and out must be 16-byte aligned, the int32/fp32
+ * arrays 4-byte aligned.  The device must be the one the plan was created
+ * on.  Reads every input, writes only `out` and the plan's workspace. */
+attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t* k_pages,
+                                 const uint8_t* v_pages, const float* kv_scales,
+                                 const int32_t* block_table, const int32_t* ctx_lens,
+                                 const int32_t* q_lens, void* out, hipStream_t stream);
+
+/* Free the workspace and the plan.  The caller must first make sure no
+ * forward using the plan is still running (synchronise its stream).
+ * A null plan is accepted and ignored. */
+attn_status_t attn_plan_destroy(attn_plan_t plan);
+
+/* Fill *info with the plan's choices. */
+attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info);
+
+/* Static, never-null text for a status code. */
+const char* attn_status_string(attn_status_t status);
+
+/* The hipError_t (as int) of the last ATTN_ERR_HIP returned on this thread. */
+int attn_last_hip_error(void);
+
+/* ---- checking hooks: they run the same device address and FP8 decode code
+ * as the attention kernels, so the gathered bytes can be compared bit for bit
+ * with the oracle's gather. ---- */
+
+/* For every sequence b < B, kv head h, token t < max_ctx_len:
+ *   k_out[b][h][t][:], v_out[b][h][t][:]  the token's D K/V bytes (0 for t >= L_b)
+ *   scale_out[0|1][b][h][t]               its K/V page scale (0 for t >= L_b)
+ *   page_out[b][t]                        its physical page (-1 for t >= L_b)
+ * Output buffers are caller-owned device memory of exactly those shapes. */
+attn_status_t attn_debug_gather(attn_plan_t plan, const uint8_t* k_pages, const uint8_t* v_pages,
+                                const float* kv_scales, const int32_t* block_table,
+                                const int32_t* ctx_lens, uint8_t* k_out, uint8_t* v_out,
+                                float* scale_out, int32_t* page_out, hipStream_t stream);
+
+/* out[i] = the value of E4M3 byte in[i] as the attention kernels decode it
+ * (FP8 -> bf16, widened exactly to fp32).  n >= 0; n == 0 enqueues nothing. */
+attn_status_t attn_debug_decode_fp8(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

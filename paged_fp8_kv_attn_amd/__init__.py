@@ -1,0 +1,18 @@
+"""MI355X (gfx950) paged FP8-KV attention.
+
+The compute runs in the HIP library libpagedattn.so (C ABI in
+include/pagedattn.h); this package only loads it and marshals arguments.
+There is no CPU fallback: without the built library every call raises.
+"""
+
+from ._binding import (  # noqa: F401
+    AttnError,
+    Plan,
+    PlanInfo,
+    debug_decode_fp8,
+    debug_gather,
+    exported_symbols,
+    library_path,
+    load_library,
+    status_string,
+)

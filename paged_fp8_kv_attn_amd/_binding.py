@@ -1,0 +1,214 @@
+"""ctypes binding of libpagedattn.so: argument marshalling only.
+
+Tensors are torch tensors on the GPU; the binding passes their data pointers
+and the current HIP stream to the C ABI, which does all of the work.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpagedattn.so"
+
+ATTN_DTYPE_F32 = 0
+ATTN_DTYPE_BF16 = 1
+_DTYPES = {torch.float32: ATTN_DTYPE_F32, torch.bfloat16: ATTN_DTYPE_BF16}
+
+# names declared in include/pagedattn.h
+_FUNCTIONS = [
+    "attn_plan_create",
+    "attn_paged_forward",
+    "attn_plan_destroy",
+    "attn_plan_get_info",
+    "attn_status_string",
+    "attn_last_hip_error",
+    "attn_debug_gather",
+    "attn_debug_decode_fp8",
+]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        text = status_string(status)
+        if status == 4:
+            text += f" (hipError {load_library().attn_last_hip_error()})"
+        super().__init__(f"{what}: {text}")
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32),
+        ("max_ctx_len", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("num_kv_splits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("col_tiles", ctypes.c_int32),
+        ("dup_lo_columns", ctypes.c_int32),
+        ("cols_per_block", ctypes.c_int32),
+        ("col_blocks", ctypes.c_int32),
+        ("waves_per_group", ctypes.c_int32),
+        ("num_kv_splits", ctypes.c_int32),
+        ("tokens_per_split", ctypes.c_int32),
+        ("grid_size", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load the in-tree HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_fp8_kv_attn_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.attn_plan_create.argtypes = [ctypes.POINTER(PlanDesc), ctypes.POINTER(vp)]
+    lib.attn_plan_create.restype = i32
+    lib.attn_paged_forward.argtypes = [vp] * 10
+    lib.attn_paged_forward.restype = i32
+    lib.attn_plan_destroy.argtypes = [vp]
+    lib.attn_plan_destroy.restype = i32
+    lib.attn_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    lib.attn_plan_get_info.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = ctypes.c_int
+    lib.attn_debug_gather.argtypes = [vp] * 11
+    lib.attn_debug_gather.restype = i32
+    lib.attn_debug_decode_fp8.argtypes = [vp, vp, i64, vp]
+    lib.attn_debug_decode_fp8.restype = i32
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> dict:
+    lib = load_library()
+    return {name: hasattr(lib, name) for name in _FUNCTIONS}
+
+
+def status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise AttnError(status, what)
+
+
+def _dtype_code(dt) -> int:
+    if isinstance(dt, int):
+        return dt
+    if isinstance(dt, str):
+        return {"f32": ATTN_DTYPE_F32, "bf16": ATTN_DTYPE_BF16}[dt]
+    return _DTYPES[dt]
+
+
+class Plan:
+    """A plan: static shape, chosen tiling, and its one-time workspace."""
+
+    def __init__(self, *, num_seqs, num_q_heads, num_kv_heads, head_dim, num_pages, max_pages_per_seq,
+                 max_q_len, max_ctx_len, q_dtype="bf16", out_dtype="bf16", sm_scale=0.0, num_kv_splits=0,
+                 page_size=16, reserved=(0, 0, 0, 0)):
+        lib = load_library()
+        d = PlanDesc()
+        d.num_seqs = num_seqs
+        d.num_q_heads = num_q_heads
+        d.num_kv_heads = num_kv_heads
+        d.head_dim = head_dim
+        d.page_size = page_size
+        d.num_pages = num_pages
+        d.max_pages_per_seq = max_pages_per_seq
+        d.max_q_len = max_q_len
+        d.max_ctx_len = max_ctx_len
+        d.q_dtype = _dtype_code(q_dtype)
+        d.out_dtype = _dtype_code(out_dtype)
+        d.sm_scale = float(sm_scale)
+        d.num_kv_splits = num_kv_splits
+        for i, r in enumerate(reserved):
+            d.reserved[i] = r
+        self.desc = d
+        self._h = ctypes.c_void_p()
+        _check(lib.attn_plan_create(ctypes.byref(d), ctypes.byref(self._h)), "attn_plan_create")
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self) -> dict:
+        inf = PlanInfo()
+        _check(load_library().attn_plan_get_info(self._h, ctypes.byref(inf)), "attn_plan_get_info")
+        return inf.as_dict()
+
+    def forward(self, q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out, stream=None):
+        st = load_library().attn_paged_forward(
+            self._h, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(kv_scales), _ptr(block_table),
+            _ptr(ctx_lens), _ptr(q_lens), _ptr(out), _stream(stream))
+        _check(st, "attn_paged_forward")
+        return out
+
+    def close(self):
+        if self._h:
+            _check(load_library().attn_plan_destroy(self._h), "attn_plan_destroy")
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def debug_gather(plan: Plan, k_pages, v_pages, kv_scales, block_table, ctx_lens, k_out, v_out, scale_out,
+                 page_out, stream=None):
+    st = load_library().attn_debug_gather(plan.handle, _ptr(k_pages), _ptr(v_pages), _ptr(kv_scales),
+                                          _ptr(block_table), _ptr(ctx_lens), _ptr(k_out), _ptr(v_out),
+                                          _ptr(scale_out), _ptr(page_out), _stream(stream))
+    _check(st, "attn_debug_gather")
+
+
+def debug_decode_fp8(codes, out, stream=None):
+    st = load_library().attn_debug_decode_fp8(_ptr(codes), _ptr(out), int(codes.numel()), _stream(stream))
+    _check(st, "attn_debug_decode_fp8")
+    return out

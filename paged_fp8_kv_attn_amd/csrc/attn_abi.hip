@@ -1,0 +1,302 @@
+// Host side of the C ABI (include/pagedattn.h): descriptor validation, the
+// plan's tile/split choice and one-time workspace allocation, and the
+// stream-ordered forward.
+//
+// The plan object follows the memory section of the Atlas engine article
+// (ainews.cool, "技术深度解析"): everything the forward needs is allocated
+// once up front, and the forward itself allocates nothing and never
+// synchronises the host.  Tile and split sizes are chosen from the static
+// shape once, the "block sizes adapted to sequence length and GPU" of its
+// attention section, here for gfx950 only.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/pagedattn.h"
+#include "kernel_params.h"
+
+struct attn_plan_s {
+  attn_plan_desc_t desc;
+  pa::Variant variant;
+  int device;
+  int group;
+  int cols_per_block;
+  int col_blocks;
+  int num_splits;
+  int chunks_per_split;
+  int grid;
+  float sm_scale;
+  void* workspace;
+  size_t workspace_bytes;
+  float* part_o;
+  float* part_ml;
+  int32_t* counters;
+};
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+attn_status_t hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return ATTN_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+constexpr int kChunkTokens = 32;   // keys per chunk (two pages)
+constexpr int kTargetGroups = 1024;  // workgroups wanted at the longest context: 4 per CU on 256 CUs
+
+attn_status_t validate_desc(const attn_plan_desc_t& d) {
+  for (int r : d.reserved)
+    if (r != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.num_seqs < 1 || d.num_kv_heads < 1 || d.num_q_heads < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.num_q_heads % d.num_kv_heads != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.num_pages < 1 || d.max_q_len < 1 || d.max_ctx_len < d.max_q_len) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.page_size < 1 || d.head_dim < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.max_pages_per_seq < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.q_dtype != ATTN_DTYPE_F32 && d.q_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.out_dtype != ATTN_DTYPE_F32 && d.out_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!(d.sm_scale >= 0.f) || !std::isfinite(d.sm_scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.num_kv_splits < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.page_size != pa::kPageSize) return ATTN_ERR_UNSUPPORTED;
+  if (d.head_dim != 64 && d.head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(d.max_pages_per_seq) * d.page_size < d.max_ctx_len) return ATTN_ERR_INVALID_ARGUMENT;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK: success";
+    case ATTN_ERR_INVALID_ARGUMENT: return "ATTN_ERR_INVALID_ARGUMENT: null/misaligned pointer or inconsistent descriptor";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: request outside what this build implements";
+    case ATTN_ERR_OUT_OF_MEMORY: return "ATTN_ERR_OUT_OF_MEMORY: workspace allocation failed";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: a HIP runtime call failed (see attn_last_hip_error)";
+  }
+  return "unknown attn_status_t";
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_plan) {
+  if (!desc || !out_plan) return ATTN_ERR_INVALID_ARGUMENT;
+  *out_plan = nullptr;
+  const attn_status_t st = validate_desc(*desc);
+  if (st != ATTN_OK) return st;
+  const attn_plan_desc_t& d = *desc;
+
+  attn_plan_s* p = new (std::nothrow) attn_plan_s();
+  if (!p) return ATTN_ERR_OUT_OF_MEMORY;
+  p->desc = d;
+  p->group = d.num_q_heads / d.num_kv_heads;
+  p->sm_scale = d.sm_scale > 0.f ? d.sm_scale : 1.0f / std::sqrt(static_cast<float>(d.head_dim));
+
+  // Query columns of one (sequence, kv head): G heads x up to max_q_len tokens.
+  const int64_t cols = static_cast<int64_t>(p->group) * d.max_q_len;
+  pa::Variant v{};
+  v.head_dim = d.head_dim;
+  v.q_f32 = d.q_dtype == ATTN_DTYPE_F32;
+  v.out_f32 = d.out_dtype == ATTN_DTYPE_F32;
+  if (cols <= 8) {  // hi parts of P in columns 0..7, lo parts in 8..15
+    v.col_tiles = 1;
+    v.dup_lo = true;
+    p->cols_per_block = static_cast<int>(cols);
+  } else if (cols <= 16) {
+    v.col_tiles = 1;
+    p->cols_per_block = 16;
+  } else if (cols <= 32) {
+    v.col_tiles = 2;
+    p->cols_per_block = 32;
+  } else {
+    v.col_tiles = 4;
+    p->cols_per_block = 64;
+  }
+  p->col_blocks = ceil_div(cols, p->cols_per_block);
+  p->variant = v;
+
+  // Key partitions.
+  const int64_t max_chunks = ceil_div(d.max_ctx_len, kChunkTokens);
+  const int64_t base = static_cast<int64_t>(d.num_seqs) * d.num_kv_heads * p->col_blocks;
+  int64_t splits;
+  if (d.num_kv_splits > 0) {
+    splits = d.num_kv_splits;
+  } else {
+    splits = (kTargetGroups + base - 1) / base;
+    const int64_t cap = std::max<int64_t>(1, max_chunks / (2 * pa::kWavesPerGroup));  // >= 2 chunks per wave
+    if (splits > cap) splits = cap;
+  }
+  if (splits < 1) splits = 1;
+  if (splits > max_chunks) splits = max_chunks;
+  p->chunks_per_split = ceil_div(max_chunks, splits);
+  p->num_splits = ceil_div(max_chunks, p->chunks_per_split);
+  const int64_t grid = base * p->num_splits;
+  if (grid > 0x7fffffffLL || base > 0x7fffffffLL) {
+    delete p;
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  p->grid = static_cast<int>(grid);
+
+  if (hipGetDevice(&p->device) != hipSuccess) {
+    delete p;
+    return hip_fail(hipGetLastError());
+  }
+  p->workspace = nullptr;
+  p->workspace_bytes = 0;
+  p->part_o = nullptr;
+  p->part_ml = nullptr;
+  p->counters = nullptr;
+  if (p->num_splits > 1) {
+    // partials of every (sequence, kv head, column block, partition) and one
+    // arrival counter per (sequence, kv head, column block); the counters are
+    // zeroed here once and re-armed by the kernel itself
+    const size_t rows = static_cast<size_t>(grid) * p->cols_per_block;
+    const size_t o_bytes = rows * d.head_dim * sizeof(float);
+    const size_t ml_bytes = rows * 2 * sizeof(float);
+    const size_t cnt_bytes = static_cast<size_t>(base) * sizeof(int32_t);
+    p->workspace_bytes = o_bytes + ml_bytes + cnt_bytes;
+    hipError_t e = hipMalloc(&p->workspace, p->workspace_bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      delete p;
+      return e == hipErrorOutOfMemory ? ATTN_ERR_OUT_OF_MEMORY : hip_fail(e);
+    }
+    p->part_o = static_cast<float*>(p->workspace);
+    p->part_ml = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + o_bytes);
+    p->counters = reinterpret_cast<int32_t*>(static_cast<char*>(p->workspace) + o_bytes + ml_bytes);
+    e = hipMemset(p->counters, 0, cnt_bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      (void)hipFree(p->workspace);
+      delete p;
+      return hip_fail(e);
+    }
+  }
+  *out_plan = p;
+  return ATTN_OK;
+}
+
+attn_status_t attn_plan_destroy(attn_plan_t plan) {
+  if (!plan) return ATTN_OK;
+  attn_status_t st = ATTN_OK;
+  if (plan->workspace) {
+    const hipError_t e = hipFree(plan->workspace);
+    if (e != hipSuccess) st = hip_fail(e);
+  }
+  delete plan;
+  return st;
+}
+
+attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info) {
+  if (!plan || !info) return ATTN_ERR_INVALID_ARGUMENT;
+  info->col_tiles = plan->variant.col_tiles;
+  info->dup_lo_columns = plan->variant.dup_lo ? 1 : 0;
+  info->cols_per_block = plan->cols_per_block;
+  info->col_blocks = plan->col_blocks;
+  info->waves_per_group = pa::kWavesPerGroup;
+  info->num_kv_splits = plan->num_splits;
+  info->tokens_per_split = plan->chunks_per_split * kChunkTokens;
+  info->grid_size = plan->grid;
+  info->workspace_bytes = plan->workspace_bytes;
+  return ATTN_OK;
+}
+
+static attn_status_t check_device(const attn_plan_s* plan) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return hip_fail(hipGetLastError());
+  return dev == plan->device ? ATTN_OK : ATTN_ERR_INVALID_ARGUMENT;
+}
+
+attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t* k_pages, const uint8_t* v_pages,
+                                 const float* kv_scales, const int32_t* block_table, const int32_t* ctx_lens,
+                                 const int32_t* q_lens, void* out, hipStream_t stream) {
+  if (!plan || !q || !k_pages || !v_pages || !kv_scales || !block_table || !ctx_lens || !q_lens || !out)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16) ||
+      !aligned(kv_scales, 4) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) || !aligned(q_lens, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  const attn_status_t dst = check_device(plan);
+  if (dst != ATTN_OK) return dst;
+
+  const attn_plan_desc_t& d = plan->desc;
+  pa::StreamParams sp{};
+  sp.q = q;
+  sp.k_pages = k_pages;
+  sp.v_pages = v_pages;
+  sp.kv_scales = kv_scales;
+  sp.block_table = block_table;
+  sp.ctx_lens = ctx_lens;
+  sp.q_lens = q_lens;
+  sp.out = out;
+  sp.part_o = plan->part_o;
+  sp.part_ml = plan->part_ml;
+  sp.counters = plan->counters;
+  sp.num_seqs = d.num_seqs;
+  sp.num_q_heads = d.num_q_heads;
+  sp.num_kv_heads = d.num_kv_heads;
+  sp.group = plan->group;
+  sp.bt_stride = d.max_pages_per_seq;
+  sp.max_q_len = d.max_q_len;
+  sp.cols_per_block = plan->cols_per_block;
+  sp.col_blocks = plan->col_blocks;
+  sp.num_splits = plan->num_splits;
+  sp.chunks_per_split = plan->chunks_per_split;
+  sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
+  sp.qk_scale_log2 = plan->sm_scale * 1.4426950408889634f;
+
+  const hipError_t e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+attn_status_t attn_debug_gather(attn_plan_t plan, const uint8_t* k_pages, const uint8_t* v_pages,
+                                const float* kv_scales, const int32_t* block_table, const int32_t* ctx_lens,
+                                uint8_t* k_out, uint8_t* v_out, float* scale_out, int32_t* page_out,
+                                hipStream_t stream) {
+  if (!plan || !k_pages || !v_pages || !kv_scales || !block_table || !ctx_lens || !k_out || !v_out ||
+      !scale_out || !page_out)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(kv_scales, 4) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) || !aligned(scale_out, 4) ||
+      !aligned(page_out, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  const attn_status_t dst = check_device(plan);
+  if (dst != ATTN_OK) return dst;
+  const attn_plan_desc_t& d = plan->desc;
+  pa::GatherParams gp{};
+  gp.k_pages = k_pages;
+  gp.v_pages = v_pages;
+  gp.kv_scales = kv_scales;
+  gp.block_table = block_table;
+  gp.ctx_lens = ctx_lens;
+  gp.k_out = k_out;
+  gp.v_out = v_out;
+  gp.scale_out = scale_out;
+  gp.page_out = page_out;
+  gp.num_seqs = d.num_seqs;
+  gp.num_kv_heads = d.num_kv_heads;
+  gp.head_dim = d.head_dim;
+  gp.bt_stride = d.max_pages_per_seq;
+  gp.max_ctx_len = d.max_ctx_len;
+  gp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
+  const hipError_t e = pa::launch_debug_gather(gp, stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+attn_status_t attn_debug_decode_fp8(const uint8_t* in, float* out, int64_t n, hipStream_t stream) {
+  if (n < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (n == 0) return ATTN_OK;
+  if (!in || !out || !aligned(out, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  const hipError_t e = pa::launch_debug_decode(in, out, n, stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+}  // extern "C"

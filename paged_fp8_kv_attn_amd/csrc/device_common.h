@@ -1,0 +1,57 @@
+// Device helpers shared by the attention kernels and the checking hooks, so
+// that the hooks exercise exactly the address arithmetic and FP8 decode the
+// attention kernels run.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernel_params.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Byte offset of the (page, kv head) chunk in k_pages / v_pages: a chunk is
+// the 16 tokens x D bytes of one head inside one page.
+__device__ __forceinline__ uint64_t chunk_offset(int32_t page, int head, int num_kv_heads, int head_dim) {
+  return ((uint64_t)(uint32_t)page * (uint64_t)num_kv_heads + (uint64_t)head) * (uint64_t)(kPageSize * head_dim);
+}
+
+// K chunk: token-major, byte of (slot, d) at slot * D + d.
+__device__ __forceinline__ uint32_t k_in_chunk(int slot, int d, int head_dim) {
+  return (uint32_t)(slot * head_dim + d);
+}
+
+// V chunk: four consecutive slots interleaved per d, byte of (slot, d) at
+// ((slot / 4) * D + d) * 4 + slot % 4.
+__device__ __forceinline__ uint32_t v_in_chunk(int slot, int d, int head_dim) {
+  return (uint32_t)((((slot >> 2) * head_dim) + d) * 4 + (slot & 3));
+}
+
+// Two FP8 E4M3 bytes of `w` (bytes 0,1 or, with HI, bytes 2,3) -> two bf16,
+// exactly: every E4M3 value is a bf16 value.  gfx950's converter reads the
+// OCP E4M3 encoding; the scale operand 1.0 leaves values unchanged.
+template <bool HI>
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+
+// Eight FP8 bytes (w0 bytes 0..3, then w1 bytes 0..3) -> eight bf16 in order.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = fp8x2_to_bf16x2<false>(w0);
+  const bf16x2 b = fp8x2_to_bf16x2<true>(w0);
+  const bf16x2 c = fp8x2_to_bf16x2<false>(w1);
+  const bf16x2 d = fp8x2_to_bf16x2<true>(w1);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+}  // namespace pa

@@ -1,0 +1,71 @@
+// Parameter blocks passed by value from the host launcher to the kernels,
+// and the launcher entry points (defined next to their kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kPageSize = 16;  // tokens per page
+
+struct StreamParams {
+  const void* q;               // [sum Q][Hq][D] bf16 or fp32
+  const uint8_t* k_pages;      // [P][Hkv][16][D]
+  const uint8_t* v_pages;      // [P][Hkv][4][D][4]
+  const float* kv_scales;      // [2][P][Hkv]
+  const int32_t* block_table;  // [B][bt_stride]
+  const int32_t* ctx_lens;     // [B]
+  const int32_t* q_lens;       // [B]
+  void* out;                   // [sum Q][Hq][D] bf16 or fp32
+  float* part_o;               // [items][cols_per_block][D] unnormalised partial outputs
+  float* part_ml;              // [items][cols_per_block][2] running max (log2 units), sum
+  int32_t* counters;           // [B * Hkv * col_blocks] finished partitions; zero between forwards
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;               // Hq / Hkv
+  int32_t bt_stride;           // max_pages_per_seq
+  int32_t max_q_len;
+  int32_t cols_per_block;      // query columns (new token x head of a group) per workgroup
+  int32_t col_blocks;          // workgroups along the columns of one (sequence, kv head)
+  int32_t num_splits;          // partitions along the keys
+  int32_t chunks_per_split;    // 32-key chunks per partition
+  int64_t v_scale_offset;      // P * Hkv: start of the V scales in kv_scales
+  float qk_scale_log2;         // sm_scale * log2(e)
+};
+
+struct Variant {
+  int head_dim;     // 64 or 128
+  int col_tiles;    // 1, 2 or 4 MFMA column tiles of 16
+  bool dup_lo;      // low halves of P in spare columns (col_tiles == 1, <= 8 columns)
+  bool q_f32;
+  bool out_f32;
+};
+
+constexpr int kWavesPerGroup = 4;
+
+hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream);
+
+struct GatherParams {
+  const uint8_t* k_pages;
+  const uint8_t* v_pages;
+  const float* kv_scales;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  uint8_t* k_out;
+  uint8_t* v_out;
+  float* scale_out;
+  int32_t* page_out;
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t bt_stride;
+  int32_t max_ctx_len;
+  int64_t v_scale_offset;
+};
+
+hipError_t launch_debug_gather(const GatherParams& p, hipStream_t stream);
+hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
+
+}  // namespace pa
