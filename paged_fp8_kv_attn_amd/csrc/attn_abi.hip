@@ -35,7 +35,7 @@ struct attn_plan_s {
   size_t workspace_bytes;
   float* part_o;
   float* part_ml;
-  int32_t* counters;
+  int merge_grid;
 };
 
 namespace {
@@ -155,17 +155,14 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   p->workspace_bytes = 0;
   p->part_o = nullptr;
   p->part_ml = nullptr;
-  p->counters = nullptr;
+  p->merge_grid = p->num_splits > 1 ? static_cast<int>(base) : 0;
   if (p->num_splits > 1) {
-    // partials of every (sequence, kv head, column block, partition) and one
-    // arrival counter per (sequence, kv head, column block); the counters are
-    // zeroed here once and re-armed by the kernel itself
+    // partials of every (sequence, kv head, column block, partition)
     const size_t rows = static_cast<size_t>(grid) * p->cols_per_block;
     const size_t o_bytes = rows * d.head_dim * sizeof(float);
     const size_t ml_bytes = rows * 2 * sizeof(float);
-    const size_t cnt_bytes = static_cast<size_t>(base) * sizeof(int32_t);
-    p->workspace_bytes = o_bytes + ml_bytes + cnt_bytes;
-    hipError_t e = hipMalloc(&p->workspace, p->workspace_bytes);
+    p->workspace_bytes = o_bytes + ml_bytes;
+    const hipError_t e = hipMalloc(&p->workspace, p->workspace_bytes);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       delete p;
@@ -173,14 +170,6 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
     }
     p->part_o = static_cast<float*>(p->workspace);
     p->part_ml = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + o_bytes);
-    p->counters = reinterpret_cast<int32_t*>(static_cast<char*>(p->workspace) + o_bytes + ml_bytes);
-    e = hipMemset(p->counters, 0, cnt_bytes);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) {
-      (void)hipFree(p->workspace);
-      delete p;
-      return hip_fail(e);
-    }
   }
   *out_plan = p;
   return ATTN_OK;
@@ -240,7 +229,6 @@ attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t*
   sp.out = out;
   sp.part_o = plan->part_o;
   sp.part_ml = plan->part_ml;
-  sp.counters = plan->counters;
   sp.num_seqs = d.num_seqs;
   sp.num_q_heads = d.num_q_heads;
   sp.num_kv_heads = d.num_kv_heads;
@@ -254,7 +242,8 @@ attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t*
   sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
   sp.qk_scale_log2 = plan->sm_scale * 1.4426950408889634f;
 
-  const hipError_t e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream);
+  hipError_t e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream);
+  if (e == hipSuccess && plan->merge_grid > 0) e = pa::launch_split_merge(plan->variant, sp, plan->merge_grid, stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

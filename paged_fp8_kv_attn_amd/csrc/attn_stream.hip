@@ -29,7 +29,8 @@
 //     straight from the S^T accumulator layout.  The 4-token interleave of
 //     the V page layout makes each lane's operand 32 contiguous bytes.
 // Waves then merge their (m, l, O) through LDS; a workgroup writes the final
-// output, or an unnormalised partial for the log-sum-exp split merge.
+// output, or an unnormalised partial that a second small kernel merges by
+// log-sum-exp with the other partitions of its (sequence, kv head).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -249,46 +250,71 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
   const uint8_t* kpool = p.k_pages;
   const uint8_t* vpool = p.v_pages;
 
-  // ---- chunk loop, one chunk of prefetch --------------------------------
+  // ---- chunk loop --------------------------------------------------------
+  // This wave's chunks are c_k = c_begin + wave + k * NW, k < nk.  The block
+  // table entries and the K/V page scales of the next 32 chunks are fetched
+  // by one gather (lane j: chunk k0 + j/2, page j%2) and read with readlane,
+  // so the loop never waits on a scalar memory load.  K/V bytes of chunk
+  // k+1 are in flight while chunk k is computed.
+  const int nk = (c_begin + wave < c_end) ? (c_end - c_begin - wave + NW - 1) / NW : 0;
+  int32_t bt_v = 0;
+  float sk_v = 0.f, sv_v = 0.f;
+  auto load_batch = [&](int k0) {
+    const int k = k0 + (lane >> 1);
+    int32_t ph = 0;
+    float a = 0.f, bsc = 0.f;
+    if (k < nk) {
+      const int c = c_begin + wave + k * NW;
+      const int pg = min(2 * c + (lane & 1), npages - 1);  // a missing second page repeats the first
+      ph = bt[pg];
+      const int64_t sidx = (int64_t)ph * p.num_kv_heads + h;
+      a = p.kv_scales[sidx];
+      bsc = p.kv_scales[p.v_scale_offset + sidx];
+    }
+    bt_v = ph;
+    sk_v = a;
+    sv_v = bsc;
+  };
   u32x4 kr[2][GD::NKV], vr[2][GD::NVV];
-  float sk[2], sv[2];
-  auto load_chunk = [&](int c, u32x4 (&kdst)[2][GD::NKV], u32x4 (&vdst)[2][GD::NVV], float (&skd)[2],
-                        float (&svd)[2]) {
-    const int pg0 = 2 * c;
-    const int pg1 = min(pg0 + 1, npages - 1);
-    const int32_t ph0 = bt[pg0];
-    const int32_t ph1 = (pg0 + 1 < npages) ? bt[pg1] : ph0;
-    const int32_t phys[2] = {ph0, ph1};
+  auto load_kv = [&](int k) {
+    const int slot = 2 * (k & 31);
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
-      const uint64_t base = chunk_offset(phys[pg], h, p.num_kv_heads, D);
+      const int32_t ph = __builtin_amdgcn_readlane(bt_v, slot + pg);
+      const uint64_t base = chunk_offset(ph, h, p.num_kv_heads, D);
       const u32x4* kp = reinterpret_cast<const u32x4*>(kpool + base + koff);
       const u32x4* vp = reinterpret_cast<const u32x4*>(vpool + base + voff);
 #pragma unroll
-      for (int i = 0; i < GD::NKV; ++i) kdst[pg][i] = __builtin_nontemporal_load(kp + i);
+      for (int i = 0; i < GD::NKV; ++i) kr[pg][i] = __builtin_nontemporal_load(kp + i);
 #pragma unroll
-      for (int i = 0; i < GD::NVV; ++i) vdst[pg][i] = __builtin_nontemporal_load(vp + i);
-      const int64_t sidx = (int64_t)phys[pg] * p.num_kv_heads + h;
-      skd[pg] = p.kv_scales[sidx];
-      svd[pg] = p.kv_scales[p.v_scale_offset + sidx];
+      for (int i = 0; i < GD::NVV; ++i) vr[pg][i] = __builtin_nontemporal_load(vp + i);
     }
   };
 
-  int c = c_begin + wave;
-  if (c < c_end) load_chunk(c, kr, vr, sk, sv);
-  for (; c < c_end; c += NW) {
+  if (nk > 0) {
+    load_batch(0);
+    load_kv(0);
+  }
+  for (int k = 0; k < nk; ++k) {
+    const int c = c_begin + wave + k * NW;
     u32x4 kc[2][GD::NKV], vc[2][GD::NVV];
-    float skc[2], svc[2];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
 #pragma unroll
       for (int i = 0; i < GD::NKV; ++i) kc[pg][i] = kr[pg][i];
 #pragma unroll
       for (int i = 0; i < GD::NVV; ++i) vc[pg][i] = vr[pg][i];
-      skc[pg] = sk[pg];
-      svc[pg] = sv[pg];
     }
-    if (c + NW < c_end) load_chunk(c + NW, kr, vr, sk, sv);
+    const int slot = 2 * (k & 31);
+    float skc[2], svc[2];
+    skc[0] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sk_v), slot));
+    skc[1] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sk_v), slot + 1));
+    svc[0] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sv_v), slot));
+    svc[1] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sv_v), slot + 1));
+    if (k + 1 < nk) {
+      if (((k + 1) & 31) == 0) load_batch(k + 1);
+      load_kv(k + 1);
+    }
 
     // S^T = K Q^T for both pages
     f32x4 sacc[2][NCT];
@@ -507,26 +533,33 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
       }
     }
   }
-  if (final_out) return;
-
-  // Publish the partial at device scope, then count the partitions that have
-  // finished; the last one to arrive merges all of them (in split order, so
-  // the result does not depend on arrival order) and re-arms the counter.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  __shared__ int s_last;
-  if (threadIdx.x == 0) {
-    int* cnt = p.counters + item_id / p.num_splits;
-    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (prev == nsplit_here - 1) ? 1 : 0;
-    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  merge_partials<D, OUTF32>(p, (size_t)(item_id - split), nsplit_here, cols_here, col0, row0, h);
 }
+
+// One workgroup per (sequence, kv head, column block) whose keys were split:
+// merges its partitions' partials in split order.  Launched right after the
+// attention kernel on the same stream.
+template <int D, bool OUTF32>
+__global__ __launch_bounds__(256) void split_merge_kernel(StreamParams p) {
+  int item = blockIdx.x;
+  const int cb = item % p.col_blocks;
+  item /= p.col_blocks;
+  const int h = item % p.num_kv_heads;
+  const int b = item / p.num_kv_heads;
+  const int L = p.ctx_lens[b];
+  const int Qb = p.q_lens[b];
+  const int G = p.group;
+  const int ncols = G * Qb;
+  const int col0 = cb * p.cols_per_block;
+  if (col0 >= ncols) return;
+  const int cols_here = min(p.cols_per_block, ncols - col0);
+  const int i_hi = (col0 + cols_here - 1) / G;
+  const int nchunks = (L - Qb + i_hi + 1 + 31) >> 5;
+  const int nsplit = (nchunks + p.chunks_per_split - 1) / p.chunks_per_split;
+  if (nsplit <= 1) return;  // the attention kernel wrote this block's output itself
+  const int row0 = (p.max_q_len == 1) ? b : prefix_rows(p.q_lens, b, threadIdx.x & 63);
+  merge_partials<D, OUTF32>(p, (size_t)blockIdx.x * p.num_splits, nsplit, cols_here, col0, row0, h);
+}
+
 
 // ---- dispatch --------------------------------------------------------------
 
@@ -560,6 +593,21 @@ hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int 
   if (v.head_dim == 128) return launch_tiles<128>(v, p, grid, stream);
   if (v.head_dim == 64) return launch_tiles<64>(v, p, grid, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  const dim3 block(256);
+  if (v.head_dim == 128) {
+    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<128, true>), dim3(grid), block, 0, stream, p);
+    else hipLaunchKernelGGL((split_merge_kernel<128, false>), dim3(grid), block, 0, stream, p);
+  } else if (v.head_dim == 64) {
+    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<64, true>), dim3(grid), block, 0, stream, p);
+    else hipLaunchKernelGGL((split_merge_kernel<64, false>), dim3(grid), block, 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace pa

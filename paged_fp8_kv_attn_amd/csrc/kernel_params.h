@@ -20,7 +20,6 @@ struct StreamParams {
   void* out;                   // [sum Q][Hq][D] bf16 or fp32
   float* part_o;               // [items][cols_per_block][D] unnormalised partial outputs
   float* part_ml;              // [items][cols_per_block][2] running max (log2 units), sum
-  int32_t* counters;           // [B * Hkv * col_blocks] finished partitions; zero between forwards
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -46,6 +45,7 @@ struct Variant {
 constexpr int kWavesPerGroup = 4;
 
 hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream);
+hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream);
 
 struct GatherParams {
   const uint8_t* k_pages;
