@@ -3,8 +3,9 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
 A step is one forward of the whole path (block-table gather, FP8 dequant,
-GQA QK^T, online softmax, PV, partition merge -- one kernel launch) over one
-batch of synthetic input.  Default workload: the LLaMA-3-8B-shaped decode
+GQA QK^T, online softmax, PV in the attention kernel; log-sum-exp merge of
+split segments in a second, small kernel) over one batch of synthetic
+input.  Default workload: the LLaMA-3-8B-shaped decode
 batch (32 sequences, 32 query / 8 KV heads, head_dim 128, contexts uniform in
 512..4096, FP8 E4M3 KV in 16-token pages of a shuffled pool).  Inputs are
 resident in HBM before timing starts; each forward reads a different copy of
@@ -12,9 +13,11 @@ the KV pool from a rotation set of >= 1 GiB so that neither L2 nor the
 256 MB Infinity Cache can serve the KV.  Forwards are launched as one HIP
 graph of K nodes (``--eager`` launches them one by one from Python).
 
-Prints one JSON line (rank 0): metric/value (KV-path HBM GB/s), query
-tokens/s, the roofline of the attention kernel, and the CPU oracle's rate on
-a bounded sample of the same workload (``cpu_baseline``).
+Prints one JSON line (rank 0): metric/value (algorithmic HBM GB/s of the
+whole step), query tokens/s, the roofline of the attention kernel (its own
+duration, from HIP events the library records around it on the forward's
+stream), and the CPU oracle's rate on a bounded sample of the same workload
+(``cpu_baseline``).
 """
 
 from __future__ import annotations
@@ -81,21 +84,108 @@ def workload_config(w) -> dict:
 
 
 def source_hash() -> str:
+    """Hash of the attention kernel's source, so a counter summary taken on an
+    older kernel is not applied to a newer one."""
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def counter_summary_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"attn_stream_kernel_{workload}_hbm_counters.txt")
+
+
 def committed_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source; otherwise None."""
-    path = os.path.join(PROFILES, f"attn_stream_{workload}_hbm_traffic.json")
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE per dispatch, each
+    scaled by what the same counter reads for a plain device copy of known
+    size), if it was taken on the current kernel source; otherwise None."""
+    path = counter_summary_path(workload)
     if not os.path.exists(path):
         return None
+    vals = {}
     with open(path) as f:
-        d = json.load(f)
-    if d.get("kernel_source_sha256_16") != source_hash():
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    try:
+        fetch = float(vals["attn_FETCH_SIZE_KiB_per_dispatch"])
+        write = float(vals["attn_WRITE_SIZE_KiB_per_dispatch"])
+        copy_bytes = float(vals["copy_bytes"])
+        cf = float(vals["copy_FETCH_SIZE_KiB_per_dispatch"])
+        cw = float(vals["copy_WRITE_SIZE_KiB_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+    return fetch * (copy_bytes / cf) + write * (copy_bytes / cw)
+
+
+class HipGraph:
+    """A HIP graph captured in global capture mode straight through the HIP
+    runtime (only library calls run inside the capture), so that the event
+    records the library makes around its attention kernel become event nodes
+    of the graph."""
+
+    def __init__(self):
+        import ctypes
+
+        self._c = ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        vp = ctypes.c_void_p
+        hip.hipStreamBeginCapture.argtypes = [vp, ctypes.c_int]
+        hip.hipStreamEndCapture.argtypes = [vp, ctypes.POINTER(vp)]
+        hip.hipGraphInstantiate.argtypes = [ctypes.POINTER(vp), vp, vp, vp, ctypes.c_size_t]
+        hip.hipGraphLaunch.argtypes = [vp, vp]
+        hip.hipGraphExecDestroy.argtypes = [vp]
+        hip.hipGraphDestroy.argtypes = [vp]
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        hip.hipEventDestroy.argtypes = [vp]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self._hip = hip
+        self._graph = vp()
+        self._exec = vp()
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with hipError {rc}")
+
+    def capture(self, stream, body):
+        c = self._c
+        st = c.c_void_p(stream.cuda_stream)
+        self._ok(self._hip.hipStreamBeginCapture(st, 0), "hipStreamBeginCapture")  # global mode
+        try:
+            body()
+        finally:
+            rc = self._hip.hipStreamEndCapture(st, c.byref(self._graph))
+        self._ok(rc, "hipStreamEndCapture")
+        self._ok(self._hip.hipGraphInstantiate(c.byref(self._exec), self._graph, None, None, 0),
+                 "hipGraphInstantiate")
+
+    def launch(self, stream):
+        self._ok(self._hip.hipGraphLaunch(self._exec, self._c.c_void_p(stream.cuda_stream)), "hipGraphLaunch")
+
+    def event(self):
+        """A timing-enabled hipEvent_t made by the HIP runtime itself."""
+        e = self._c.c_void_p()
+        self._ok(self._hip.hipEventCreateWithFlags(self._c.byref(e), 0), "hipEventCreateWithFlags")
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self._c.c_float(0)
+        self._ok(self._hip.hipEventElapsedTime(self._c.byref(ms), a, b), "hipEventElapsedTime")
+        return float(ms.value)
+
+    def destroy_event(self, e):
+        self._hip.hipEventDestroy(e)
+
+    def close(self):
+        if self._exec:
+            self._hip.hipGraphExecDestroy(self._exec)
+            self._exec = self._c.c_void_p()
+        if self._graph:
+            self._hip.hipGraphDestroy(self._graph)
+            self._graph = self._c.c_void_p()
 
 
 def cpu_baseline(w, counts, budget_s: float) -> dict:
@@ -226,25 +316,27 @@ def main():
 
     graph = None
     if not args.eager:
-        graph = torch.cuda.CUDAGraph()
+        graph = HipGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            graph.capture_begin()
+        torch.cuda.synchronize()
+
+        def body():
             for i in range(args.steps):
                 k, v, s = pools[i % copies]
                 plan.forward(q, k, v, s, bt, ctx, ql, out, stream=cap)
-            graph.capture_end()
-        stream.wait_stream(cap)
-        graph.replay()  # one untimed replay of the captured steps
+
+        graph.capture(cap, body)
+        graph.launch(stream)  # one untimed launch of the captured steps
         torch.cuda.synchronize()
 
+    # Timed region 1: the K steps (one graph launch, or eager launches).
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     if graph is not None:
-        graph.replay()
+        graph.launch(stream)
     else:
         for i in range(args.steps):
             fwd(i)
@@ -253,18 +345,51 @@ def main():
     total_ms = e0.elapsed_time(e1)
     ms = total_ms / args.steps
 
+    # Timed region 2: the same K steps launched one by one, each with a pair
+    # of HIP events that the library records on the forward's stream just
+    # before and just after its attention kernel.  A sleep kernel queued in
+    # front gives the host time to enqueue every step before the GPU reaches
+    # them, so no host latency falls between an event and its kernel.
+    hipt = HipGraph()
+    k_start = [hipt.event() for _ in range(args.steps)]
+    k_stop = [hipt.event() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    cal0 = torch.cuda.Event(enable_timing=True)
+    cal1 = torch.cuda.Event(enable_timing=True)
+    cal0.record(stream)
+    torch.cuda._sleep(1 << 20)
+    cal1.record(stream)
+    torch.cuda.synchronize()
+    sleep_ms_per_unit = cal0.elapsed_time(cal1) / (1 << 20)
+    head_start_ms = 5.0 + 0.05 * args.steps  # generous: ~50 us of host time per step
+    torch.cuda._sleep(int(head_start_ms / max(sleep_ms_per_unit, 1e-9)))
+    for i in range(args.steps):
+        plan.set_kernel_events(k_start[i], k_stop[i])
+        fwd(i)
+    plan.set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    kernel_ms = [hipt.elapsed_ms(a, b) for a, b in zip(k_start, k_stop)]
+    for e in k_start + k_stop:
+        hipt.destroy_event(e)
+    attn_ms = float(np.mean(kernel_ms))
+
     gbs = counts["bytes"] / (ms * 1e-3) / 1e9
     tflops = counts["flops"] / (ms * 1e-3) / 1e12
     qtok = counts["query_tokens"] / (ms * 1e-3)
+    k_gbs = counts["bytes"] / (attn_ms * 1e-3) / 1e9
+    k_tflops = counts["flops"] / (attn_ms * 1e-3) / 1e12
     prefill_like = counts["flops"] / max(1, counts["bytes"]) > 312  # above the bf16 ridge point
     traffic = committed_traffic(w.name)
     if prefill_like:
-        roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
+        roof = {"bound": "mfma", "achieved": k_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": k_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
     else:
-        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}
-    roof.update({"kernel": "attn_stream_kernel", "algorithmic_bytes_per_launch": counts["bytes"],
+        roof = {"bound": "hbm", "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": k_gbs / HBM_PEAK_GBS, "traffic": traffic}
+    roof.update({"kernel": "attn_stream_kernel", "kernel_avg_us": attn_ms * 1e3,
+                 "kernel_median_us": float(np.median(kernel_ms)) * 1e3,
+                 "kernel_min_us": float(np.min(kernel_ms)) * 1e3, "kernel_max_us": float(np.max(kernel_ms)) * 1e3,
+                 "algorithmic_bytes_per_launch": counts["bytes"],
                  "algorithmic_flops_per_launch": counts["flops"], "launches_per_step": 1})
 
     res = {
@@ -298,6 +423,9 @@ def main():
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(line + "\n")
+    hipt.close()
+    if graph is not None:
+        graph.close()
     plan.close()
 
 

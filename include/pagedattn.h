@@ -97,23 +97,30 @@ typedef struct {
   attn_dtype_t q_dtype;      /* BF16 or F32 */
   attn_dtype_t out_dtype;    /* BF16 or F32 */
   float sm_scale;            /* softmax scale; 0 means 1/sqrt(head_dim) */
-  int32_t num_kv_splits;     /* 0: plan chooses; n >= 1: split each sequence's
-                                keys into at most n partitions merged by
-                                log-sum-exp */
+  int32_t num_kv_splits;     /* 0: plan chooses; n >= 1: the keys of all
+                                (sequence, kv head, column block) segments are
+                                cut into segments * n equal contiguous
+                                partitions (so each of equal-length segments
+                                gets exactly n), merged by log-sum-exp */
   int32_t reserved[4];       /* must be zero */
 } attn_plan_desc_t;
 
-/* What the plan chose (for tests and measurement). */
+/* What the plan chose (for tests and measurement).  A segment is one
+ * (sequence, kv head, block of query columns) with the keys its columns see,
+ * cut into 32-key chunks; the chunks of all segments, laid end to end, are
+ * shared equally by the grid_size workgroups of the attention kernel. */
 typedef struct {
-  int32_t col_tiles;        /* 16-column MFMA tiles per workgroup (1, 2 or 4) */
-  int32_t dup_lo_columns;   /* 1: low parts of P ride in spare MFMA columns */
-  int32_t cols_per_block;   /* query columns (token x head of a group) per workgroup */
-  int32_t col_blocks;       /* workgroups along the query columns of a group */
-  int32_t waves_per_group;  /* waves per workgroup */
-  int32_t num_kv_splits;    /* partitions per (sequence, kv head, column block) */
-  int32_t tokens_per_split; /* keys per partition (multiple of 32) */
-  int32_t grid_size;        /* workgroups of the attention kernel */
-  size_t workspace_bytes;   /* device bytes owned by the plan */
+  int32_t col_tiles;              /* 16-column MFMA tiles per workgroup (1, 2 or 4) */
+  int32_t dup_lo_columns;         /* 1: low parts of P ride in spare MFMA columns */
+  int32_t cols_per_block;         /* query columns (token x head of a group) per segment */
+  int32_t col_blocks;             /* segments along the query columns of a group */
+  int32_t waves_per_group;        /* waves per workgroup */
+  int32_t num_segments;           /* B * Hkv * col_blocks */
+  int32_t grid_size;              /* workgroups of the attention kernel */
+  int32_t merge_grid_size;        /* workgroups of the merge kernel (0: not launched) */
+  int32_t resident_groups_per_cu; /* attention workgroups one compute unit holds at once */
+  int32_t compute_units;          /* of the plan's device */
+  size_t workspace_bytes;         /* device bytes owned by the plan */
 } attn_plan_info_t;
 
 /* Validate desc, choose tiles/splits, allocate the workspace once with
@@ -138,6 +145,15 @@ attn_status_t attn_plan_destroy(attn_plan_t plan);
 
 /* Fill *info with the plan's choices. */
 attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info);
+
+/* Measurement hook.  With both events non-null, every later forward on this
+ * plan records `attention_start` on its stream just before the attention
+ * kernel and `attention_stop` just after it (before the merge kernel), so
+ * hipEventElapsedTime gives that kernel's duration.  Both null turns it off;
+ * exactly one null is ATTN_ERR_INVALID_ARGUMENT.  The events stay owned by
+ * the caller and must outlive their use. */
+attn_status_t attn_plan_set_kernel_events(attn_plan_t plan, hipEvent_t attention_start,
+                                          hipEvent_t attention_stop);
 
 /* Static, never-null text for a status code. */
 const char* attn_status_string(attn_status_t status);

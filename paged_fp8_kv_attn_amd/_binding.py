@@ -24,6 +24,7 @@ _FUNCTIONS = [
     "attn_paged_forward",
     "attn_plan_destroy",
     "attn_plan_get_info",
+    "attn_plan_set_kernel_events",
     "attn_status_string",
     "attn_last_hip_error",
     "attn_debug_gather",
@@ -66,9 +67,11 @@ class PlanInfo(ctypes.Structure):
         ("cols_per_block", ctypes.c_int32),
         ("col_blocks", ctypes.c_int32),
         ("waves_per_group", ctypes.c_int32),
-        ("num_kv_splits", ctypes.c_int32),
-        ("tokens_per_split", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32),
         ("grid_size", ctypes.c_int32),
+        ("merge_grid_size", ctypes.c_int32),
+        ("resident_groups_per_cu", ctypes.c_int32),
+        ("compute_units", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -101,6 +104,8 @@ def load_library():
     lib.attn_plan_destroy.restype = i32
     lib.attn_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.attn_plan_get_info.restype = i32
+    lib.attn_plan_set_kernel_events.argtypes = [vp, vp, vp]
+    lib.attn_plan_set_kernel_events.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -180,6 +185,21 @@ class Plan:
         inf = PlanInfo()
         _check(load_library().attn_plan_get_info(self._h, ctypes.byref(inf)), "attn_plan_get_info")
         return inf.as_dict()
+
+    def set_kernel_events(self, start=None, stop=None):
+        """Record events `start`/`stop` (raw hipEvent_t handles as ints or
+        c_void_p, or objects with a `cuda_event` handle) around the attention
+        kernel of every later forward (None, None: stop recording)."""
+        def ev(e):
+            if e is None:
+                return None
+            if isinstance(e, ctypes.c_void_p):
+                return e
+            if isinstance(e, int):
+                return ctypes.c_void_p(e)
+            return ctypes.c_void_p(e.cuda_event)
+        _check(load_library().attn_plan_set_kernel_events(self._h, ev(start), ev(stop)),
+               "attn_plan_set_kernel_events")
 
     def forward(self, q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out, stream=None):
         st = load_library().attn_paged_forward(

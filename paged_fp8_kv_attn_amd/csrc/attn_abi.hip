@@ -27,15 +27,20 @@ struct attn_plan_s {
   int group;
   int cols_per_block;
   int col_blocks;
-  int num_splits;
-  int chunks_per_split;
-  int grid;
+  int num_segments;  // (sequence, kv head, column block) units
+  int grid;          // attention workgroups sharing the key chunks
+  int occupancy;     // resident attention workgroups per compute unit
+  int num_cus;
   float sm_scale;
   void* workspace;
   size_t workspace_bytes;
   float* part_o;
   float* part_ml;
+  int64_t* seq_chunk0;
+  int32_t* seq_row0;
   int merge_grid;
+  hipEvent_t ev_start;  // optional: recorded around the attention kernel
+  hipEvent_t ev_stop;
 };
 
 namespace {
@@ -51,8 +56,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
-constexpr int kChunkTokens = 32;   // keys per chunk (two pages)
-constexpr int kTargetGroups = 1024;  // workgroups wanted at the longest context: 4 per CU on 256 CUs
+constexpr int kChunkTokens = 32;  // keys per chunk (two pages)
+constexpr int kMinChunksPerGroup = 16;  // a workgroup's share is at least 4 chunks per wave
 
 attn_status_t validate_desc(const attn_plan_desc_t& d) {
   for (int r : d.reserved)
@@ -125,52 +130,85 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   p->col_blocks = ceil_div(cols, p->cols_per_block);
   p->variant = v;
 
-  // Key partitions.
-  const int64_t max_chunks = ceil_div(d.max_ctx_len, kChunkTokens);
-  const int64_t base = static_cast<int64_t>(d.num_seqs) * d.num_kv_heads * p->col_blocks;
-  int64_t splits;
-  if (d.num_kv_splits > 0) {
-    splits = d.num_kv_splits;
-  } else {
-    splits = (kTargetGroups + base - 1) / base;
-    const int64_t cap = std::max<int64_t>(1, max_chunks / (2 * pa::kWavesPerGroup));  // >= 2 chunks per wave
-    if (splits > cap) splits = cap;
-  }
-  if (splits < 1) splits = 1;
-  if (splits > max_chunks) splits = max_chunks;
-  p->chunks_per_split = ceil_div(max_chunks, splits);
-  p->num_splits = ceil_div(max_chunks, p->chunks_per_split);
-  const int64_t grid = base * p->num_splits;
-  if (grid > 0x7fffffffLL || base > 0x7fffffffLL) {
+  p->num_segments = 0;
+  p->workspace = nullptr;
+  p->workspace_bytes = 0;
+  p->part_o = nullptr;
+  p->part_ml = nullptr;
+  p->seq_chunk0 = nullptr;
+  p->seq_row0 = nullptr;
+  p->ev_start = nullptr;
+  p->ev_stop = nullptr;
+  const int64_t segments = static_cast<int64_t>(d.num_seqs) * d.num_kv_heads * p->col_blocks;
+  if (segments > 0x3fffffffLL) {
     delete p;
     return ATTN_ERR_UNSUPPORTED;
   }
-  p->grid = static_cast<int>(grid);
+  p->num_segments = static_cast<int>(segments);
+  if (segments * p->cols_per_block > 0x3fffffffLL) {
+    delete p;
+    return ATTN_ERR_UNSUPPORTED;
+  }
 
   if (hipGetDevice(&p->device) != hipSuccess) {
     delete p;
     return hip_fail(hipGetLastError());
   }
-  p->workspace = nullptr;
-  p->workspace_bytes = 0;
-  p->part_o = nullptr;
-  p->part_ml = nullptr;
-  p->merge_grid = p->num_splits > 1 ? static_cast<int>(base) : 0;
-  if (p->num_splits > 1) {
-    // partials of every (sequence, kv head, column block, partition)
-    const size_t rows = static_cast<size_t>(grid) * p->cols_per_block;
-    const size_t o_bytes = rows * d.head_dim * sizeof(float);
-    const size_t ml_bytes = rows * 2 * sizeof(float);
-    p->workspace_bytes = o_bytes + ml_bytes;
-    const hipError_t e = hipMalloc(&p->workspace, p->workspace_bytes);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      delete p;
-      return e == hipErrorOutOfMemory ? ATTN_ERR_OUT_OF_MEMORY : hip_fail(e);
-    }
-    p->part_o = static_cast<float*>(p->workspace);
-    p->part_ml = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + o_bytes);
+  // Workgroups of the attention kernel: by default as many as the GPU keeps
+  // resident at once (every one then streams an equal share of the chunks in
+  // a single round), and no more than one per kMinChunksPerGroup chunks of
+  // the largest lengths, so that small problems are not split at all.
+  hipError_t e = hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e == hipSuccess) e = pa::stream_attention_occupancy(v, &p->occupancy);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e);
   }
+  if (p->occupancy < 1) p->occupancy = 1;
+  const int64_t max_chunks = segments * ceil_div(d.max_ctx_len, kChunkTokens);
+  int64_t grid;
+  if (d.num_kv_splits > 0) {
+    grid = segments * d.num_kv_splits;
+  } else {
+    // wide column tiles hold one workgroup per compute unit: queue several
+    const int per_cu = v.col_tiles > 1 ? std::max(p->occupancy, 4) : p->occupancy;
+    grid = static_cast<int64_t>(p->num_cus) * per_cu;
+    grid = std::min<int64_t>(grid, std::max<int64_t>(1, max_chunks / kMinChunksPerGroup));
+  }
+  grid = std::min<int64_t>(grid, max_chunks);
+  grid = std::max<int64_t>(grid, 1);
+  if (grid > 0x3fffffffLL) {
+    delete p;
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  p->grid = static_cast<int>(grid);
+  // merge: one workgroup per (segment, query column of its block)
+  p->merge_grid = p->grid > 1 ? p->num_segments * p->cols_per_block : 0;
+
+  // Workspace, allocated once: partial slots (segments + grid of them, one
+  // per (segment, workgroup) pair that can occur), and where each sequence
+  // starts in the chunk list.
+  const size_t slots = static_cast<size_t>(segments) + static_cast<size_t>(grid);
+  const size_t o_bytes = slots * p->cols_per_block * d.head_dim * sizeof(float);
+  const size_t ml_bytes = slots * p->cols_per_block * 2 * sizeof(float);
+  const size_t c0_bytes = (static_cast<size_t>(d.num_seqs) + 1) * sizeof(int64_t);
+  const size_t r0_bytes = static_cast<size_t>(d.num_seqs) * sizeof(int32_t);
+  auto round_up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  p->workspace_bytes = round_up(o_bytes) + round_up(ml_bytes) + round_up(c0_bytes) + round_up(r0_bytes);
+  e = hipMalloc(&p->workspace, p->workspace_bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    delete p;
+    return e == hipErrorOutOfMemory ? ATTN_ERR_OUT_OF_MEMORY : hip_fail(e);
+  }
+  char* ws = static_cast<char*>(p->workspace);
+  p->part_o = reinterpret_cast<float*>(ws);
+  ws += round_up(o_bytes);
+  p->part_ml = reinterpret_cast<float*>(ws);
+  ws += round_up(ml_bytes);
+  p->seq_chunk0 = reinterpret_cast<int64_t*>(ws);
+  ws += round_up(c0_bytes);
+  p->seq_row0 = reinterpret_cast<int32_t*>(ws);
   *out_plan = p;
   return ATTN_OK;
 }
@@ -193,10 +231,20 @@ attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info) {
   info->cols_per_block = plan->cols_per_block;
   info->col_blocks = plan->col_blocks;
   info->waves_per_group = pa::kWavesPerGroup;
-  info->num_kv_splits = plan->num_splits;
-  info->tokens_per_split = plan->chunks_per_split * kChunkTokens;
+  info->num_segments = plan->num_segments;
   info->grid_size = plan->grid;
+  info->merge_grid_size = plan->merge_grid;
+  info->resident_groups_per_cu = plan->occupancy;
+  info->compute_units = plan->num_cus;
   info->workspace_bytes = plan->workspace_bytes;
+  return ATTN_OK;
+}
+
+attn_status_t attn_plan_set_kernel_events(attn_plan_t plan, hipEvent_t attention_start, hipEvent_t attention_stop) {
+  if (!plan) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((attention_start == nullptr) != (attention_stop == nullptr)) return ATTN_ERR_INVALID_ARGUMENT;
+  plan->ev_start = attention_start;
+  plan->ev_stop = attention_stop;
   return ATTN_OK;
 }
 
@@ -237,13 +285,24 @@ attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t*
   sp.max_q_len = d.max_q_len;
   sp.cols_per_block = plan->cols_per_block;
   sp.col_blocks = plan->col_blocks;
-  sp.num_splits = plan->num_splits;
-  sp.chunks_per_split = plan->chunks_per_split;
+  sp.seq_chunk0 = plan->seq_chunk0;
+  sp.seq_row0 = plan->seq_row0;
   sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
   sp.qk_scale_log2 = plan->sm_scale * 1.4426950408889634f;
 
-  hipError_t e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream);
-  if (e == hipSuccess && plan->merge_grid > 0) e = pa::launch_split_merge(plan->variant, sp, plan->merge_grid, stream);
+  hipError_t e = hipSuccess;
+  unsigned ev_flags = 0;
+  if (plan->ev_start) {
+    // under stream capture the records must become event nodes of the graph
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e == hipSuccess && cs == hipStreamCaptureStatusActive) ev_flags = hipEventRecordExternal;
+    if (e == hipSuccess) e = hipEventRecordWithFlags(plan->ev_start, stream, ev_flags);
+  }
+  if (e == hipSuccess) e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream);
+  if (e == hipSuccess && plan->ev_stop) e = hipEventRecordWithFlags(plan->ev_stop, stream, ev_flags);
+  if (e == hipSuccess && plan->merge_grid > 0)
+    e = pa::launch_split_merge(plan->variant, sp, plan->merge_grid, plan->grid, stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

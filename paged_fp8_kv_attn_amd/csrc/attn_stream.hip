@@ -1,17 +1,27 @@
-// Paged FP8-KV attention for gfx950: one workgroup per (sequence, kv head,
-// block of query columns, key partition), KV streamed from HBM straight into
-// MFMA operand registers.
+// Paged FP8-KV attention for gfx950: the keys of every (sequence, kv head,
+// block of query columns) are cut into 32-key chunks, the chunks of all of
+// them are laid end to end, and each workgroup streams an equal contiguous
+// range of that list, KV going from HBM straight into MFMA operand registers.
 //
 // Follows the attention section of the Atlas engine article (ainews.cool,
-// "技术深度解析": a FlashAttention-2 variant with dedicated MQA/GQA kernels),
-// its quantisation section (FP8 with per-group scales folded into the
-// kernel) and the paged FP8 KV cache of the GB10 article (ainews.surl.tw).
+// "技术深度解析": a FlashAttention-2 variant with dedicated MQA/GQA kernels and
+// tiling adapted to sequence length and GPU), its quantisation section (FP8
+// with per-group scales folded into the kernel) and the paged FP8 KV cache of
+// the GB10 article (ainews.surl.tw).
 //
 // Shape of the work.  The G = Hq/Hkv query heads of a kv head, times the Q_b
 // new tokens of a sequence, form G*Q_b "query columns" that all read the same
-// keys.  A workgroup owns up to 16*col_tiles of them (decode: the G heads;
-// MTP verification: 5 tokens x G heads; prefill: a slice of tokens x G) and a
-// partition of the keys.  Its 4 waves take 32-key chunks (two pages) in turn.
+// keys.  A segment is one (sequence, kv head, block of up to 16*col_tiles
+// columns) with its keys; it owns n = ceil(kv_end / 32) chunks.  Segments are
+// ordered (sequence, kv head, column block) and workgroup w of W takes global
+// chunks [floor(w T / W), floor((w+1) T / W)) of the T in total, so every
+// workgroup does the same amount of streaming whatever the length mix.  A
+// workgroup walks the pieces of segments in its range; its 4 waves take the
+// chunks of a piece in turn and merge through LDS at the piece's end.  A
+// segment that lies inside one workgroup's range is written to `out`
+// directly; otherwise each workgroup writes an unnormalised partial into slot
+// (segment + w), unique because ranges and segments are both ordered, and
+// the merge kernel combines them by log-sum-exp.
 //
 // Per chunk, in each wave (lane = 16*lq + ln):
 //   * K: lane reads 32 (D=128) contiguous bytes of token slot ln at
@@ -28,9 +38,6 @@
 //   * O^T += V^T * P~^T: A = V^T (rows = d, k = the 32 keys), B = P~^T taken
 //     straight from the S^T accumulator layout.  The 4-token interleave of
 //     the V page layout makes each lane's operand 32 contiguous bytes.
-// Waves then merge their (m, l, O) through LDS; a workgroup writes the final
-// output, or an unnormalised partial that a second small kernel merges by
-// log-sum-exp with the other partitions of its (sequence, kv head).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,6 +59,7 @@ struct Geo {
 };
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kChunk = 32;  // keys per chunk (two pages)
 
 __device__ __forceinline__ float max_over_lq(float x) {
   // maximum over the four lanes ln, ln+16, ln+32, ln+48
@@ -68,22 +76,6 @@ __device__ __forceinline__ float sum_over_lq(float x) {
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  // Workgroups are handed to the 8 XCDs round-robin; map consecutive logical
-  // items onto one XCD so items sharing a kv head share that XCD's L2.
-  const int per = n >> 3;
-  if (bid >= (per << 3)) return bid;
-  return (bid & 7) * per + (bid >> 3);
-}
-
-__device__ __forceinline__ int prefix_rows(const int32_t* q_lens, int b, int lane) {
-  int acc = 0;
-  for (int k = lane; k < b; k += 64) acc += q_lens[k];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  return __builtin_amdgcn_readfirstlane(acc);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -108,89 +100,161 @@ __device__ __forceinline__ void split_q_f32(const float* x, bf16x8& p1, bf16x8& 
   }
 }
 
-}  // namespace
+// ---- schedule ------------------------------------------------------------
 
-// ---- log-sum-exp merge of key partitions --------------------------------
-// out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s,  m = max_s m_s,
-// over the partials of one (sequence, kv head, column block), in split order.
-template <int D, bool OUTF32>
-__device__ __forceinline__ void merge_partials(const StreamParams& p, size_t item0, int nsplit, int cols_here,
-                                               int col0, int row0, int h) {
-  constexpr int V4 = D / 4;
-  const int G = p.group;
-  for (int e = threadIdx.x; e < cols_here * V4; e += blockDim.x) {
-    const int rc = e / V4;
-    const int d4 = (e - rc * V4) * 4;
-    float mx = kNegInf;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, p.part_ml[((item0 + s) * p.cols_per_block + rc) * 2]);
-    const float base = (mx == kNegInf) ? 0.f : mx;
-    float lsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-      const size_t ri = (item0 + s) * p.cols_per_block + rc;
-      const float w = __builtin_amdgcn_exp2f(p.part_ml[ri * 2] - base);
-      lsum += w * p.part_ml[ri * 2 + 1];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_o + ri * D + d4);
-      acc += v * w;
-    }
-    const float inv = 1.f / lsum;
-    const int gc = col0 + rc;
-    const int i = gc / G;
-    const int g = gc - i * G;
-    const size_t off = ((size_t)(row0 + i) * p.num_q_heads + h * G + g) * D + d4;
-    if constexpr (OUTF32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = acc * inv;
-    } else {
-      const uint32_t w0 = pack_bf16(acc[0] * inv, acc[1] * inv);
-      const uint32_t w1 = pack_bf16(acc[2] * inv, acc[3] * inv);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) = make_uint2(w0, w1);
-    }
-  }
+// Chunks of segment (sequence with L keys and Q new tokens, column block cb):
+// the keys visible to at least one of its columns, in 32-key chunks.
+__device__ __forceinline__ int seg_chunks(int L, int Q, int G, int cpb, int cb) {
+  const int ncols = G * Q;
+  const int col0 = cb * cpb;
+  if (col0 >= ncols) return 0;
+  const int i_hi = (min(col0 + cpb, ncols) - 1) / G;
+  return (L - Q + i_hi + 1 + kChunk - 1) / kChunk;
 }
 
-template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32>
-__global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(StreamParams p) {
+// Chunks of one kv head of a sequence: all of its column blocks.
+__device__ __forceinline__ int head_chunks(const StreamParams& p, int L, int Q) {
+  if (p.col_blocks == 1) return seg_chunks(L, Q, p.group, p.cols_per_block, 0);
+  int s = 0;
+  for (int cb = 0; cb < p.col_blocks; ++cb) s += seg_chunks(L, Q, p.group, p.cols_per_block, cb);
+  return s;
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Lengths of sequence b and its chunk count over all kv heads (zeros for
+// b >= B).  Lane i of a wave holds sequence base + i.
+struct SeqLens {
+  int L, Q;
+  int64_t nb;
+};
+
+__device__ __forceinline__ SeqLens load_seq(const StreamParams& p, int b) {
+  SeqLens c{0, 0, 0};
+  if (b < p.num_seqs) {
+    c.L = p.ctx_lens[b];
+    c.Q = p.q_lens[b];
+    c.nb = (int64_t)p.num_kv_heads * head_chunks(p, c.L, c.Q);
+  }
+  return c;
+}
+
+// Where sequence b starts: its first global chunk and first query row.
+struct SeqStart {
+  int b;
+  int64_t chunk0;
+  int row0;
+  int L, Q;
+};
+
+// Total chunks over all sequences (wave-uniform); `c0` holds the first 64.
+__device__ int64_t total_chunks(const StreamParams& p, int lane, const SeqLens& c0) {
+  int64_t total = wave_sum64(c0.nb);
+  for (int base = 64; base < p.num_seqs; base += 64) total += wave_sum64(load_seq(p, base + lane).nb);
+  return total;
+}
+
+// The sequence whose chunks contain global chunk `pos` (< total).
+__device__ SeqStart locate_seq(const StreamParams& p, int64_t pos, int lane, const SeqLens& c0) {
+  int64_t carry = 0;
+  int rows = 0;
+  for (int base = 0; base < p.num_seqs; base += 64) {
+    const SeqLens c = (base == 0) ? c0 : load_seq(p, base + lane);
+    const int64_t incl = wave_incl_scan64(c.nb, lane);
+    const int qincl = (int)wave_incl_scan64(c.Q, lane);
+    const int64_t start = carry + incl - c.nb;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(c.nb > 0 && start <= pos && pos < start + c.nb);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      SeqStart s;
+      s.b = base + src;
+      s.chunk0 = __shfl(start, src);
+      s.row0 = rows + __shfl(qincl - c.Q, src);
+      s.L = __shfl(c.L, src);
+      s.Q = __shfl(c.Q, src);
+      return s;
+    }
+    carry += __shfl(incl, 63);
+    rows += __shfl(qincl, 63);
+  }
+  SeqStart s{p.num_seqs, carry, rows, 0, 0};  // not reached for pos < total
+  return s;
+}
+
+// Workgroup 0 records where every sequence starts (and the total) for the
+// merge kernel, which runs after this kernel on the same stream.
+__device__ void write_seq_meta(const StreamParams& p, int lane) {
+  int64_t carry = 0;
+  int rows = 0;
+  for (int base = 0; base < p.num_seqs; base += 64) {
+    const int b = base + lane;
+    int64_t nb = 0;
+    int qb = 0;
+    if (b < p.num_seqs) {
+      qb = p.q_lens[b];
+      nb = (int64_t)p.num_kv_heads * head_chunks(p, p.ctx_lens[b], qb);
+    }
+    const int64_t incl = wave_incl_scan64(nb, lane);
+    const int qincl = (int)wave_incl_scan64(qb, lane);
+    if (b < p.num_seqs) {
+      p.seq_chunk0[b] = carry + incl - nb;
+      p.seq_row0[b] = rows + qincl - qb;
+    }
+    carry += __shfl(incl, 63);
+    rows += __shfl(qincl, 63);
+  }
+  if (lane == 0) p.seq_chunk0[p.num_seqs] = carry;
+}
+
+// First workgroup whose range holds global chunk g: ranges start at
+// floor(w T / W), so it is the largest w with w T < (g + 1) W.
+__device__ __forceinline__ int wg_of_chunk(int64_t g, int64_t T, int W) {
+  return (int)(((g + 1) * (int64_t)W + T - 1) / T) - 1;
+}
+
+// ---- one piece of a segment ----------------------------------------------
+
+struct PieceDesc {
+  int b, h, cb;
+  int L, Q, row0;
+  int c_begin, c_end;  // chunk range of the piece inside its segment
+  bool whole;          // the piece is the whole segment
+  int slot;            // partial slot when not whole
+};
+
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int NBUF>
+__device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc& pc, int lane, int wave) {
   using GD = Geo<D>;
   constexpr int NW = kWavesPerGroup;
   constexpr int NP = QF32 ? 3 : 1;
-  static_assert(!DUPLO || NCT == 1, "spare-column low parts need a single tile");
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane >> 4;
   const int ln = lane & 15;
-
-  // ---- work item -------------------------------------------------------
-  int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int item_id = item;
-  const int split = item % p.num_splits;
-  item /= p.num_splits;
-  const int cb = item % p.col_blocks;
-  item /= p.col_blocks;
-  const int h = item % p.num_kv_heads;
-  const int b = item / p.num_kv_heads;
-
-  const int L = p.ctx_lens[b];
-  const int Qb = p.q_lens[b];
+  const int h = pc.h;
+  const int L = pc.L;
+  const int Qb = pc.Q;
   const int G = p.group;
   const int ncols = G * Qb;
-  const int col0 = cb * p.cols_per_block;
-  if (col0 >= ncols) return;
+  const int col0 = pc.cb * p.cols_per_block;
   const int cols_here = min(p.cols_per_block, ncols - col0);
   const int i_lo = col0 / G;
-  const int i_hi = (col0 + cols_here - 1) / G;
-  const int kv_end = L - Qb + i_hi + 1;  // keys seen by at least one column here
-  const int nchunks = (kv_end + 31) >> 5;
-  const int c_begin = split * p.chunks_per_split;
-  if (c_begin >= nchunks) return;
-  const int c_end = min(c_begin + p.chunks_per_split, nchunks);
-  const int nsplit_here = (nchunks + p.chunks_per_split - 1) / p.chunks_per_split;
-  const int row0 = (p.max_q_len == 1) ? b : prefix_rows(p.q_lens, b, lane);
   const int first_masked_key = L - Qb + i_lo + 1;  // keys >= this are hidden from some column
   const int npages = (L + kPageSize - 1) / kPageSize;
 
   // ---- this lane's query columns and Q operand ----------------------------
-  int lim[NCT];        // last visible key of the lane's column (-1: unused column)
+  int lim[NCT];  // last visible key of the lane's column (-1: unused column)
   int qrow[NCT], qhead[NCT];
   bf16x8 qop[NP][NCT][GD::NSLAB];
 #pragma unroll
@@ -201,7 +265,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
     const int i = gc / G;
     const int g = gc - i * G;
     lim[t] = valid ? (L - Qb + i) : -1;
-    qrow[t] = row0 + i;
+    qrow[t] = pc.row0 + i;
     qhead[t] = h * G + g;
     const size_t qoff = ((size_t)qrow[t] * p.num_q_heads + qhead[t]) * D + (size_t)lq * GD::DQ;
     if constexpr (QF32) {
@@ -244,7 +308,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
     for (int c = 0; c < GD::NVB; ++c) o[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int32_t* bt = p.block_table + (size_t)b * p.bt_stride;
+  const int32_t* bt = p.block_table + (size_t)pc.b * p.bt_stride;
   const uint32_t koff = k_in_chunk(ln, lq * GD::DQ, D);
   const uint32_t voff = v_in_chunk(4 * lq, GD::NVB * ln, D);
   const uint8_t* kpool = p.k_pages;
@@ -252,11 +316,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
 
   // ---- chunk loop --------------------------------------------------------
   // This wave's chunks are c_k = c_begin + wave + k * NW, k < nk.  The block
-  // table entries and the K/V page scales of the next 32 chunks are fetched
+  // table entries and the K/V page scales of 32 chunks at a time are fetched
   // by one gather (lane j: chunk k0 + j/2, page j%2) and read with readlane,
-  // so the loop never waits on a scalar memory load.  K/V bytes of chunk
-  // k+1 are in flight while chunk k is computed.
-  const int nk = (c_begin + wave < c_end) ? (c_end - c_begin - wave + NW - 1) / NW : 0;
+  // so the loop never waits on a scalar memory load.  K/V bytes go into a
+  // ring of NBUF register buffers: a buffer is refilled with chunk k + NBUF
+  // as soon as chunk k has been consumed, so NBUF chunks are in flight while
+  // one is computed.  A buffer's page scales are latched when it is filled.
+  const int c_begin = pc.c_begin;
+  const int nk = (c_begin + wave < pc.c_end) ? (pc.c_end - c_begin - wave + NW - 1) / NW : 0;
   int32_t bt_v = 0;
   float sk_v = 0.f, sv_v = 0.f;
   auto load_batch = [&](int k0) {
@@ -275,8 +342,13 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
     sk_v = a;
     sv_v = bsc;
   };
-  u32x4 kr[2][GD::NKV], vr[2][GD::NVV];
-  auto load_kv = [&](int k) {
+  u32x4 kbuf[NBUF][2][GD::NKV], vbuf[NBUF][2][GD::NVV];
+  float skb[NBUF][2], svb[NBUF][2];
+  // fill ring slot j with chunk k (k < nk); a new batch of block-table
+  // entries is fetched when k starts one (every chunk before k has already
+  // been issued and has its scales latched)
+  auto issue = [&](int k, u32x4 (&kb)[2][GD::NKV], u32x4 (&vb)[2][GD::NVV], float (&skj)[2], float (&svj)[2]) {
+    if ((k & 31) == 0) load_batch(k);
     const int slot = 2 * (k & 31);
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
@@ -285,37 +357,23 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
       const u32x4* kp = reinterpret_cast<const u32x4*>(kpool + base + koff);
       const u32x4* vp = reinterpret_cast<const u32x4*>(vpool + base + voff);
 #pragma unroll
-      for (int i = 0; i < GD::NKV; ++i) kr[pg][i] = __builtin_nontemporal_load(kp + i);
+      for (int i = 0; i < GD::NKV; ++i) kb[pg][i] = __builtin_nontemporal_load(kp + i);
 #pragma unroll
-      for (int i = 0; i < GD::NVV; ++i) vr[pg][i] = __builtin_nontemporal_load(vp + i);
+      for (int i = 0; i < GD::NVV; ++i) vb[pg][i] = __builtin_nontemporal_load(vp + i);
+    }
+    // the scales are read after the KV loads are issued: waiting for them
+    // (they were fetched before) leaves the KV loads in flight
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      skj[pg] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sk_v), slot + pg));
+      svj[pg] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sv_v), slot + pg));
     }
   };
 
-  if (nk > 0) {
-    load_batch(0);
-    load_kv(0);
-  }
-  for (int k = 0; k < nk; ++k) {
+  // compute chunk k from its ring slot
+  auto step = [&](int k, const u32x4 (&kc)[2][GD::NKV], const u32x4 (&vc)[2][GD::NVV], const float (&skc)[2],
+                  const float (&svc)[2]) {
     const int c = c_begin + wave + k * NW;
-    u32x4 kc[2][GD::NKV], vc[2][GD::NVV];
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-#pragma unroll
-      for (int i = 0; i < GD::NKV; ++i) kc[pg][i] = kr[pg][i];
-#pragma unroll
-      for (int i = 0; i < GD::NVV; ++i) vc[pg][i] = vr[pg][i];
-    }
-    const int slot = 2 * (k & 31);
-    float skc[2], svc[2];
-    skc[0] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sk_v), slot));
-    skc[1] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sk_v), slot + 1));
-    svc[0] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sv_v), slot));
-    svc[1] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sv_v), slot + 1));
-    if (k + 1 < nk) {
-      if (((k + 1) & 31) == 0) load_batch(k + 1);
-      load_kv(k + 1);
-    }
-
     // S^T = K Q^T for both pages
     f32x4 sacc[2][NCT];
 #pragma unroll
@@ -338,8 +396,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
     // online softmax (log2 units)
     const float fk0 = p.qk_scale_log2 * skc[0];
     const float fk1 = p.qk_scale_log2 * skc[1];
-    const int key0 = c * 32 + 4 * lq;  // key of register j: key0 + j (page 0), key0 + 16 + j (page 1)
-    const bool need_mask = (c * 32 + 31) >= first_masked_key;
+    const int key0 = c * kChunk + 4 * lq;  // key of register j: key0 + j (page 0), key0 + 16 + j (page 1)
+    const bool need_mask = (c * kChunk + kChunk - 1) >= first_masked_key;
     uint32_t phi[NCT][4], plo[NCT][4];
     bool rescale = false;
     float alpha[NCT];
@@ -377,17 +435,17 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
       l[t] = l[t] * alpha[t] + rs;
       // P~ = p * V scale, as bf16 hi + lo
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float sc = (k < 2) ? svc[0] : svc[1];
-        const float a = pr[2 * k] * sc;
-        const float bb = pr[2 * k + 1] * sc;
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const float sc = (k2 < 2) ? svc[0] : svc[1];
+        const float a = pr[2 * k2] * sc;
+        const float bb = pr[2 * k2 + 1] * sc;
         const uint32_t hw = pack_bf16(a, bb);
         const uint32_t lw = pack_bf16(a - bf16_lo(hw), bb - bf16_hi(hw));
         if constexpr (DUPLO) {
-          phi[t][k] = lo_lane ? lw : hw;
+          phi[t][k2] = lo_lane ? lw : hw;
         } else {
-          phi[t][k] = hw;
-          plo[t][k] = lw;
+          phi[t][k2] = hw;
+          plo[t][k2] = lw;
         }
       }
     }
@@ -399,7 +457,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
     }
 
     // O^T += V^T P~^T
-    const bool tail = (c * 32 + 32) > L;
+    const bool tail = (c * kChunk + kChunk) > L;
     uint32_t vmask0 = 0xffffffffu, vmask1 = 0xffffffffu;
     if (tail) {
       vmask0 = 0u;
@@ -426,6 +484,20 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
         o[t][cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi[t], o[t][cblk], 0, 0, 0);
         if constexpr (!DUPLO)
           o[t][cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[t], o[t][cblk], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < NBUF; ++j)
+    if (j < nk) issue(j, kbuf[j], vbuf[j], skb[j], svb[j]);
+  for (int k0 = 0; k0 < nk; k0 += NBUF) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      const int k = k0 + j;
+      if (k < nk) {
+        step(k, kbuf[j], vbuf[j], skb[j], svb[j]);
+        if (k + NBUF < nk) issue(k + NBUF, kbuf[j], vbuf[j], skb[j], svb[j]);
       }
     }
   }
@@ -479,14 +551,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
     }
     __syncthreads();
   }
-  // ---- write: final output, or a partial plus the last-arriver merge ------
-  const bool final_out = (nsplit_here == 1);
+
+  // ---- write: final output, or this piece's partial -----------------------
   if (wave == 0) {
 #pragma unroll
     for (int t = 0; t < NCT; ++t) {
       const int rc = DUPLO ? ln : (16 * t + ln);
       if (rc >= cols_here || (DUPLO && ln >= 8)) continue;
-      if (final_out) {
+      if (pc.whole) {
         const float inv = 1.f / l[t];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -513,7 +585,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
           }
         }
       } else {
-        float* po = p.part_o + ((size_t)item_id * p.cols_per_block + rc) * D;
+        float* po = p.part_o + ((size_t)pc.slot * p.cols_per_block + rc) * D;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float* dst = po + GD::NVB * (4 * lq + j);
@@ -526,7 +598,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
           }
         }
         if (lq == 0) {
-          float* pm = p.part_ml + ((size_t)item_id * p.cols_per_block + rc) * 2;
+          float* pm = p.part_ml + ((size_t)pc.slot * p.cols_per_block + rc) * 2;
           pm[0] = m[t];
           pm[1] = l[t];
         }
@@ -535,75 +607,221 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void attn_stream_kernel(Stream
   }
 }
 
-// One workgroup per (sequence, kv head, column block) whose keys were split:
-// merges its partitions' partials in split order.  Launched right after the
-// attention kernel on the same stream.
-template <int D, bool OUTF32>
-__global__ __launch_bounds__(256) void split_merge_kernel(StreamParams p) {
-  int item = blockIdx.x;
-  const int cb = item % p.col_blocks;
-  item /= p.col_blocks;
-  const int h = item % p.num_kv_heads;
-  const int b = item / p.num_kv_heads;
-  const int L = p.ctx_lens[b];
-  const int Qb = p.q_lens[b];
-  const int G = p.group;
-  const int ncols = G * Qb;
-  const int col0 = cb * p.cols_per_block;
-  if (col0 >= ncols) return;
-  const int cols_here = min(p.cols_per_block, ncols - col0);
-  const int i_hi = (col0 + cols_here - 1) / G;
-  const int nchunks = (L - Qb + i_hi + 1 + 31) >> 5;
-  const int nsplit = (nchunks + p.chunks_per_split - 1) / p.chunks_per_split;
-  if (nsplit <= 1) return;  // the attention kernel wrote this block's output itself
-  const int row0 = (p.max_q_len == 1) ? b : prefix_rows(p.q_lens, b, threadIdx.x & 63);
-  merge_partials<D, OUTF32>(p, (size_t)blockIdx.x * p.num_splits, nsplit, cols_here, col0, row0, h);
+}  // namespace
+
+// ---- attention kernel: one balanced chunk range per workgroup -------------
+// A single column tile is held to 256 registers per wave (two waves per
+// SIMD, eight per compute unit, each with three 8 KB chunks in flight);
+// wider tiles keep the whole register file for their accumulators.
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32>
+__global__ __launch_bounds__(64 * kWavesPerGroup, (NCT == 1 ? 2 : 1)) void attn_stream_kernel(StreamParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = blockIdx.x;
+  const int W = gridDim.x;
+
+  if (w == 0 && wave == 0) write_seq_meta(p, lane);
+  const SeqLens c0 = load_seq(p, lane);
+  const int64_t T = total_chunks(p, lane, c0);
+  const int64_t lo = (int64_t)w * T / W;
+  const int64_t hi = (int64_t)(w + 1) * T / W;
+  if (lo >= hi) return;
+
+  // walk the segments of [lo, hi)
+  SeqStart ss = locate_seq(p, lo, lane, c0);
+  int b = ss.b;
+  int64_t seq0 = ss.chunk0;
+  int row0 = ss.row0;
+  int L = ss.L;
+  int Q = ss.Q;
+  int per_head = head_chunks(p, L, Q);
+  int64_t off = lo - seq0;
+  int h = (int)(off / per_head);
+  int r = (int)(off - (int64_t)h * per_head);
+  int cb = 0;
+  int n = seg_chunks(L, Q, p.group, p.cols_per_block, 0);
+  while (r >= n) {
+    r -= n;
+    ++cb;
+    n = seg_chunks(L, Q, p.group, p.cols_per_block, cb);
+  }
+  int64_t cur = lo;
+  while (true) {
+    const int take = (int)min((int64_t)(n - r), hi - cur);
+    PieceDesc pc;
+    pc.b = b;
+    pc.h = h;
+    pc.cb = cb;
+    pc.L = L;
+    pc.Q = Q;
+    pc.row0 = row0;
+    pc.c_begin = r;
+    pc.c_end = r + take;
+    pc.whole = (r == 0) && (take == n);
+    pc.slot = ((b * p.num_kv_heads + h) * p.col_blocks + cb) + w;
+    // ring depth: a single column tile leaves registers for three chunks in
+    // flight per wave, wider tiles for two
+    run_piece<D, NCT, DUPLO, QF32, OUTF32, (NCT == 1 ? 3 : 2)>(p, pc, lane, wave);
+    cur += take;
+    if (cur >= hi) break;
+    // next non-empty segment
+    r = 0;
+    do {
+      if (++cb == p.col_blocks) {
+        cb = 0;
+        if (++h == p.num_kv_heads) {
+          h = 0;
+          row0 += Q;
+          ++b;
+          L = p.ctx_lens[b];
+          Q = p.q_lens[b];
+        }
+      }
+      n = seg_chunks(L, Q, p.group, p.cols_per_block, cb);
+    } while (n == 0);
+  }
 }
 
+// ---- log-sum-exp merge of the partials of one segment ---------------------
+// out = sum_k 2^(m_k - m) O_k / sum_k 2^(m_k - m) l_k,  m = max_k m_k, over
+// the pieces of a segment.  One workgroup per (segment, query column): its 8
+// groups of D/4 threads take the pieces k = g, g + 8, ... and merge them
+// online (4 d values per thread), then group 0 merges the 8 group results
+// through LDS in group order.  The result depends only on the pieces, not on
+// timing.  Segments that one attention workgroup finished alone are skipped.
+constexpr int kMergeGroups = 8;
+
+template <int D, bool OUTF32>
+__global__ __launch_bounds__(kMergeGroups * (D / 4)) void split_merge_kernel(StreamParams p, int attn_grid) {
+  constexpr int V4 = D / 4;
+  const int rc = blockIdx.x % p.cols_per_block;
+  const int s = blockIdx.x / p.cols_per_block;
+  const int cb = s % p.col_blocks;
+  const int h = (s / p.col_blocks) % p.num_kv_heads;
+  const int b = s / (p.col_blocks * p.num_kv_heads);
+  const int L = p.ctx_lens[b];
+  const int Q = p.q_lens[b];
+  const int n = seg_chunks(L, Q, p.group, p.cols_per_block, cb);
+  const int G = p.group;
+  const int col0 = cb * p.cols_per_block;
+  if (n == 0 || col0 + rc >= G * Q) return;
+  const int64_t T = p.seq_chunk0[p.num_seqs];
+  int64_t g = p.seq_chunk0[b] + (int64_t)h * head_chunks(p, L, Q);
+  for (int c = 0; c < cb; ++c) g += seg_chunks(L, Q, G, p.cols_per_block, c);
+  const int w_first = wg_of_chunk(g, T, attn_grid);
+  const int w_last = wg_of_chunk(g + n - 1, T, attn_grid);
+  if (w_first == w_last) return;  // written whole by the attention kernel
+  const int nparts = w_last - w_first + 1;
+  const int slot0 = s + w_first;
+
+  const int grp = threadIdx.x / V4;
+  const int d4 = (threadIdx.x - grp * V4) * 4;
+  float mx = kNegInf;
+  float lsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int k = grp; k < nparts; k += kMergeGroups) {
+    // with more workgroups than chunks some ranges are empty: such a
+    // workgroup wrote no partial
+    const int64_t wk = w_first + k;
+    if ((wk * T) / attn_grid == ((wk + 1) * T) / attn_grid) continue;
+    const size_t ri = (size_t)(slot0 + k) * p.cols_per_block + rc;
+    const float mk = p.part_ml[ri * 2];
+    const float lk = p.part_ml[ri * 2 + 1];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_o + ri * D + d4);
+    const float mn = fmaxf(mx, mk);
+    const float base = (mn == kNegInf) ? 0.f : mn;
+    const float fo = __builtin_amdgcn_exp2f(mx - base);
+    const float fk = __builtin_amdgcn_exp2f(mk - base);
+    lsum = lsum * fo + lk * fk;
+    acc = acc * fo + v * fk;
+    mx = mn;
+  }
+  __shared__ f32x4 s_acc[kMergeGroups][V4];
+  __shared__ float s_m[kMergeGroups], s_l[kMergeGroups];
+  s_acc[grp][threadIdx.x - grp * V4] = acc;
+  if (threadIdx.x == grp * V4) {
+    s_m[grp] = mx;
+    s_l[grp] = lsum;
+  }
+  __syncthreads();
+  if (grp != 0) return;
+  float m_all = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kMergeGroups; ++j) m_all = fmaxf(m_all, s_m[j]);
+  const float base = (m_all == kNegInf) ? 0.f : m_all;
+  float l_all = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMergeGroups; ++j) {
+    const float f = __builtin_amdgcn_exp2f(s_m[j] - base);
+    l_all += s_l[j] * f;
+    o += s_acc[j][threadIdx.x] * f;
+  }
+  const float inv = 1.f / l_all;
+  const int gc = col0 + rc;
+  const int i = gc / G;
+  const int gg = gc - i * G;
+  const size_t off = ((size_t)(p.seq_row0[b] + i) * p.num_q_heads + h * G + gg) * D + d4;
+  if constexpr (OUTF32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = o * inv;
+  } else {
+    const uint32_t w0 = pack_bf16(o[0] * inv, o[1] * inv);
+    const uint32_t w1 = pack_bf16(o[2] * inv, o[3] * inv);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) = make_uint2(w0, w1);
+  }
+}
 
 // ---- dispatch --------------------------------------------------------------
 
 template <int D, int NCT, bool DUPLO>
-static hipError_t launch_d(const Variant& v, const StreamParams& p, int grid, hipStream_t stream) {
-  const dim3 block(64 * kWavesPerGroup);
-  if (v.q_f32 && v.out_f32)
-    hipLaunchKernelGGL((attn_stream_kernel<D, NCT, DUPLO, true, true>), dim3(grid), block, 0, stream, p);
-  else if (v.q_f32)
-    hipLaunchKernelGGL((attn_stream_kernel<D, NCT, DUPLO, true, false>), dim3(grid), block, 0, stream, p);
-  else if (v.out_f32)
-    hipLaunchKernelGGL((attn_stream_kernel<D, NCT, DUPLO, false, true>), dim3(grid), block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_stream_kernel<D, NCT, DUPLO, false, false>), dim3(grid), block, 0, stream, p);
-  return hipGetLastError();
+static const void* kernel_d(const Variant& v) {
+  if (v.q_f32 && v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, true>);
+  if (v.q_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, false>);
+  if (v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, true>);
+  return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false>);
 }
 
 template <int D>
-static hipError_t launch_tiles(const Variant& v, const StreamParams& p, int grid, hipStream_t stream) {
-  if (v.dup_lo) return launch_d<D, 1, true>(v, p, grid, stream);
+static const void* kernel_tiles(const Variant& v) {
+  if (v.dup_lo) return kernel_d<D, 1, true>(v);
   switch (v.col_tiles) {
-    case 1: return launch_d<D, 1, false>(v, p, grid, stream);
-    case 2: return launch_d<D, 2, false>(v, p, grid, stream);
-    case 4: return launch_d<D, 4, false>(v, p, grid, stream);
-    default: return hipErrorInvalidValue;
+    case 1: return kernel_d<D, 1, false>(v);
+    case 2: return kernel_d<D, 2, false>(v);
+    case 4: return kernel_d<D, 4, false>(v);
+    default: return nullptr;
   }
+}
+
+static const void* stream_kernel(const Variant& v) {
+  if (v.head_dim == 128) return kernel_tiles<128>(v);
+  if (v.head_dim == 64) return kernel_tiles<64>(v);
+  return nullptr;
+}
+
+hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu) {
+  const void* f = stream_kernel(v);
+  if (!f) return hipErrorInvalidValue;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, 64 * kWavesPerGroup, 0);
 }
 
 hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  if (v.head_dim == 128) return launch_tiles<128>(v, p, grid, stream);
-  if (v.head_dim == 64) return launch_tiles<64>(v, p, grid, stream);
-  return hipErrorInvalidValue;
+  const void* f = stream_kernel(v);
+  if (!f) return hipErrorInvalidValue;
+  void* args[] = {const_cast<StreamParams*>(&p)};
+  return hipLaunchKernel(f, dim3(grid), dim3(64 * kWavesPerGroup), args, 0, stream);
 }
 
-hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream) {
+hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, int attn_grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  const dim3 block(256);
+  const dim3 block(kMergeGroups * (v.head_dim / 4));
   if (v.head_dim == 128) {
-    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<128, true>), dim3(grid), block, 0, stream, p);
-    else hipLaunchKernelGGL((split_merge_kernel<128, false>), dim3(grid), block, 0, stream, p);
+    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<128, true>), dim3(grid), block, 0, stream, p, attn_grid);
+    else hipLaunchKernelGGL((split_merge_kernel<128, false>), dim3(grid), block, 0, stream, p, attn_grid);
   } else if (v.head_dim == 64) {
-    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<64, true>), dim3(grid), block, 0, stream, p);
-    else hipLaunchKernelGGL((split_merge_kernel<64, false>), dim3(grid), block, 0, stream, p);
+    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<64, true>), dim3(grid), block, 0, stream, p, attn_grid);
+    else hipLaunchKernelGGL((split_merge_kernel<64, false>), dim3(grid), block, 0, stream, p, attn_grid);
   } else {
     return hipErrorInvalidValue;
   }

@@ -18,8 +18,10 @@ struct StreamParams {
   const int32_t* ctx_lens;     // [B]
   const int32_t* q_lens;       // [B]
   void* out;                   // [sum Q][Hq][D] bf16 or fp32
-  float* part_o;               // [items][cols_per_block][D] unnormalised partial outputs
-  float* part_ml;              // [items][cols_per_block][2] running max (log2 units), sum
+  float* part_o;               // [slots][cols_per_block][D] unnormalised partial outputs
+  float* part_ml;              // [slots][cols_per_block][2] running max (log2 units), sum
+  int64_t* seq_chunk0;         // [B + 1] first global chunk of each sequence; [B] = total
+  int32_t* seq_row0;           // [B] first query row of each sequence
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -27,9 +29,7 @@ struct StreamParams {
   int32_t bt_stride;           // max_pages_per_seq
   int32_t max_q_len;
   int32_t cols_per_block;      // query columns (new token x head of a group) per workgroup
-  int32_t col_blocks;          // workgroups along the columns of one (sequence, kv head)
-  int32_t num_splits;          // partitions along the keys
-  int32_t chunks_per_split;    // 32-key chunks per partition
+  int32_t col_blocks;          // column blocks of one (sequence, kv head)
   int64_t v_scale_offset;      // P * Hkv: start of the V scales in kv_scales
   float qk_scale_log2;         // sm_scale * log2(e)
 };
@@ -44,8 +44,14 @@ struct Variant {
 
 constexpr int kWavesPerGroup = 4;
 
+// Attention kernel: `grid` workgroups share the key chunks of all segments
+// equally.  Partial slots needed: segments + grid.
 hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream);
-hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream);
+// Resident workgroups per compute unit for the variant's attention kernel.
+hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu);
+// Merge kernel: one workgroup per segment (`grid` = segments), for an
+// attention launch of `attn_grid` workgroups.
+hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, int attn_grid, hipStream_t stream);
 
 struct GatherParams {
   const uint8_t* k_pages;
