@@ -346,10 +346,10 @@ def main():
     ms = total_ms / args.steps
 
     # Timed region 2: the same K steps launched one by one, each with a pair
-    # of HIP events that the library records on the forward's stream just
-    # before and just after its attention kernel.  A sleep kernel queued in
-    # front gives the host time to enqueue every step before the GPU reaches
-    # them, so no host latency falls between an event and its kernel.
+    # of HIP events that the library attaches to its attention kernel's own
+    # dispatch (they take that kernel's start and end timestamps).  A sleep
+    # kernel queued in front lets the host enqueue every step before the GPU
+    # reaches them, so the steps run back to back as in region 1.
     hipt = HipGraph()
     k_start = [hipt.event() for _ in range(args.steps)]
     k_stop = [hipt.event() for _ in range(args.steps)]

@@ -147,11 +147,12 @@ attn_status_t attn_plan_destroy(attn_plan_t plan);
 attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info);
 
 /* Measurement hook.  With both events non-null, every later forward on this
- * plan records `attention_start` on its stream just before the attention
- * kernel and `attention_stop` just after it (before the merge kernel), so
- * hipEventElapsedTime gives that kernel's duration.  Both null turns it off;
- * exactly one null is ATTN_ERR_INVALID_ARGUMENT.  The events stay owned by
- * the caller and must outlive their use. */
+ * plan launches its attention kernel with `attention_start` and
+ * `attention_stop` attached to the kernel's own dispatch (hipExtLaunchKernel),
+ * so hipEventElapsedTime gives that kernel's duration alone (the merge kernel
+ * that may follow is not included).  Both null turns it off; exactly one null
+ * is ATTN_ERR_INVALID_ARGUMENT.  The events stay owned by the caller and must
+ * outlive their use; forwards under stream capture should not set them. */
 attn_status_t attn_plan_set_kernel_events(attn_plan_t plan, hipEvent_t attention_start,
                                           hipEvent_t attention_stop);
 

@@ -290,17 +290,7 @@ attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t*
   sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
   sp.qk_scale_log2 = plan->sm_scale * 1.4426950408889634f;
 
-  hipError_t e = hipSuccess;
-  unsigned ev_flags = 0;
-  if (plan->ev_start) {
-    // under stream capture the records must become event nodes of the graph
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(stream, &cs);
-    if (e == hipSuccess && cs == hipStreamCaptureStatusActive) ev_flags = hipEventRecordExternal;
-    if (e == hipSuccess) e = hipEventRecordWithFlags(plan->ev_start, stream, ev_flags);
-  }
-  if (e == hipSuccess) e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream);
-  if (e == hipSuccess && plan->ev_stop) e = hipEventRecordWithFlags(plan->ev_stop, stream, ev_flags);
+  hipError_t e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream, plan->ev_start, plan->ev_stop);
   if (e == hipSuccess && plan->merge_grid > 0)
     e = pa::launch_split_merge(plan->variant, sp, plan->merge_grid, plan->grid, stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);

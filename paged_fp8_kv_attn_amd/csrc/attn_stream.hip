@@ -39,6 +39,7 @@
 //     straight from the S^T accumulator layout.  The 4-token interleave of
 //     the V page layout makes each lane's operand 32 contiguous bytes.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -805,11 +806,16 @@ hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, 64 * kWavesPerGroup, 0);
 }
 
-hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream) {
+hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream,
+                                   hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (grid <= 0) return hipSuccess;
   const void* f = stream_kernel(v);
   if (!f) return hipErrorInvalidValue;
   void* args[] = {const_cast<StreamParams*>(&p)};
+  if (ev_start) {
+    // the events take the timestamps of this kernel's own dispatch
+    return hipExtLaunchKernel(f, dim3(grid), dim3(64 * kWavesPerGroup), args, 0, stream, ev_start, ev_stop, 0);
+  }
   return hipLaunchKernel(f, dim3(grid), dim3(64 * kWavesPerGroup), args, 0, stream);
 }
 

@@ -46,7 +46,9 @@ constexpr int kWavesPerGroup = 4;
 
 // Attention kernel: `grid` workgroups share the key chunks of all segments
 // equally.  Partial slots needed: segments + grid.
-hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream);
+// With ev_start/ev_stop non-null they record the kernel's own start and end.
+hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream,
+                                   hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // Resident workgroups per compute unit for the variant's attention kernel.
 hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu);
 // Merge kernel: one workgroup per segment (`grid` = segments), for an
