@@ -29,9 +29,13 @@
  *
  * Memory layouts (all buffers are device memory, caller-owned):
  *   q           [sum Q_b][Hq][D]  ATTN_DTYPE_BF16 or ATTN_DTYPE_F32
- *   k_pages     uint8 [P][Hkv][16][D]        token-major within (page, head)
- *   v_pages     uint8 [P][Hkv][4][D][4]      inside a (page, head): the
- *               byte of slot s, dim d sits at ((s/4)*D + d)*4 + s%4
+ *   k_pages     uint8 [P][Hkv][D/16][16][16] inside a (page, head): 16-byte
+ *               blocks of d, slot-major within a block; the byte of slot s,
+ *               dim d sits at ((d/16)*16 + s)*16 + d%16
+ *   v_pages     uint8 [P][Hkv][4][D/64][16][4][4] inside a (page, head): four
+ *               consecutive slots interleaved per d; with NVB = D/16 and
+ *               d = NVB*a + 4*i + e, the byte of slot s, dim d sits at
+ *               ((((s/4)*(D/64) + i)*16 + a)*4 + e)*4 + s%4
  *   kv_scales   fp32  [2][P][Hkv]            [0] K scales, [1] V scales
  *   block_table int32 [B][max_pages_per_seq] physical page ids
  *   ctx_lens    int32 [B]   L_b (counts the Q_b new tokens, whose K/V are
@@ -108,7 +112,8 @@ typedef struct {
 /* What the plan chose (for tests and measurement).  A segment is one
  * (sequence, kv head, block of query columns) with the keys its columns see,
  * cut into 32-key chunks; the chunks of all segments, laid end to end, are
- * shared equally by the grid_size workgroups of the attention kernel. */
+ * shared equally by the work units of the attention kernel (its waves in the
+ * packed layout, its workgroups otherwise). */
 typedef struct {
   int32_t col_tiles;              /* 16-column MFMA tiles per workgroup (1, 2 or 4) */
   int32_t dup_lo_columns;         /* 1: low parts of P ride in spare MFMA columns */
@@ -118,6 +123,10 @@ typedef struct {
   int32_t num_segments;           /* B * Hkv * col_blocks */
   int32_t grid_size;              /* workgroups of the attention kernel */
   int32_t merge_grid_size;        /* workgroups of the merge kernel (0: not launched) */
+  int32_t work_units;             /* units sharing the chunks at most: waves when packed,
+                                     workgroups otherwise */
+  int32_t packed;                 /* 1: at most 4 query columns, four pages per score tile,
+                                     one wave per chunk range */
   int32_t resident_groups_per_cu; /* attention workgroups one compute unit holds at once */
   int32_t compute_units;          /* of the plan's device */
   size_t workspace_bytes;         /* device bytes owned by the plan */

@@ -18,9 +18,12 @@ The definition followed:
 
 Readings where the pages are silent (each listed in the design notes):
   * GQA grouping: query head hq uses kv head hq // (Hq / Hkv).
-  * Layouts: k_pages [P][Hkv][S][D]; v_pages [P][Hkv][S/4][D][4], i.e. the
-    byte of token slot s at dim d of a (page, head) sits at
-    ((s // 4) * D + d) * 4 + s % 4.
+  * Layouts (the library's ABI, S = 16 slots per page):
+      k_pages [P][Hkv][D/16][S][16]: the K byte of slot s, dim d of a (page,
+        head) is k[p][h][d // 16][s][d % 16];
+      v_pages [P][Hkv][S/4][D/64][16][4][4]: with NVB = D/16 and
+        d = NVB*a + 4*i + e, the V byte of slot s, dim d is
+        v[p][h][s // 4][i][a][e][s % 4].
   * Scale 1/sqrt(D) unless given; no soft-cap, ALiBi, window or sinks.
   * Bytes past a sequence's length and unreferenced pages are never read.
 
@@ -54,12 +57,15 @@ def token_location(block_table_row: np.ndarray, t: np.ndarray, page_size: int):
 
 def k_token_bytes(k_pages: np.ndarray, pages: np.ndarray, h: int, slots: np.ndarray) -> np.ndarray:
     """K bytes of (page, head h, slot) for each token: [T][D]."""
-    return k_pages[pages, h, slots, :]
+    blocks = k_pages[pages, h, :, slots, :]  # [T][D/16][16]: d = 16 * block + offset
+    return blocks.reshape(blocks.shape[0], -1)
 
 
 def v_token_bytes(v_pages: np.ndarray, pages: np.ndarray, h: int, slots: np.ndarray) -> np.ndarray:
-    """V bytes of (page, head h, slot) for each token: [T][D] (4-token interleave)."""
-    return v_pages[pages, h, slots // 4, :, slots % 4]
+    """V bytes of (page, head h, slot) for each token: [T][D] (4-slot interleave)."""
+    parts = v_pages[pages, h, slots // 4, :, :, :, slots % 4]  # [T][i][a][e]
+    # d = NVB * a + 4 * i + e: order the axes (a, i, e)
+    return parts.transpose(0, 2, 1, 3).reshape(parts.shape[0], -1)
 
 
 def softmax_scale(head_dim: int, sm_scale: float | None) -> float:
@@ -79,7 +85,8 @@ def gather_sequence(k_pages, v_pages, kv_scales, block_table_row, ctx_len: int) 
     """Follow one sequence's block table and collect its L tokens' bytes and scales."""
     k_pages = np.asarray(k_pages)
     v_pages = np.asarray(v_pages)
-    _, hkv, page_size, d = k_pages.shape
+    _, hkv, d_blocks, page_size, _ = k_pages.shape
+    d = 16 * d_blocks
     t = np.arange(int(ctx_len))
     pages, slots = token_location(np.asarray(block_table_row).astype(np.int64), t, page_size)
     kb = np.empty((hkv, t.size, d), dtype=np.uint8)

@@ -70,6 +70,8 @@ class PlanInfo(ctypes.Structure):
         ("num_segments", ctypes.c_int32),
         ("grid_size", ctypes.c_int32),
         ("merge_grid_size", ctypes.c_int32),
+        ("work_units", ctypes.c_int32),
+        ("packed", ctypes.c_int32),
         ("resident_groups_per_cu", ctypes.c_int32),
         ("compute_units", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),

@@ -28,7 +28,8 @@ struct attn_plan_s {
   int cols_per_block;
   int col_blocks;
   int num_segments;  // (sequence, kv head, column block) units
-  int grid;          // attention workgroups sharing the key chunks
+  int grid;          // attention workgroups
+  int max_units;     // waves (packed) or workgroups sharing the key chunks
   int occupancy;     // resident attention workgroups per compute unit
   int num_cus;
   float sm_scale;
@@ -38,6 +39,7 @@ struct attn_plan_s {
   float* part_ml;
   int64_t* seq_chunk0;
   int32_t* seq_row0;
+  int2* seg_info;
   int merge_grid;
   hipEvent_t ev_start;  // optional: recorded around the attention kernel
   hipEvent_t ev_stop;
@@ -58,6 +60,7 @@ int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
 constexpr int kChunkTokens = 32;  // keys per chunk (two pages)
 constexpr int kMinChunksPerGroup = 16;  // a workgroup's share is at least 4 chunks per wave
+constexpr int kMinChunksPerWave = 8;    // a wave's share in the packed layout (matches the kernel)
 
 attn_status_t validate_desc(const attn_plan_desc_t& d) {
   for (int r : d.reserved)
@@ -113,7 +116,11 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   v.head_dim = d.head_dim;
   v.q_f32 = d.q_dtype == ATTN_DTYPE_F32;
   v.out_f32 = d.out_dtype == ATTN_DTYPE_F32;
-  if (cols <= 8) {  // hi parts of P in columns 0..7, lo parts in 8..15
+  if (cols <= 4) {  // four pages per score tile
+    v.col_tiles = 1;
+    v.packed = true;
+    p->cols_per_block = static_cast<int>(cols);
+  } else if (cols <= 8) {  // hi parts of P in columns 0..7, lo parts in 8..15
     v.col_tiles = 1;
     v.dup_lo = true;
     p->cols_per_block = static_cast<int>(cols);
@@ -137,6 +144,7 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   p->part_ml = nullptr;
   p->seq_chunk0 = nullptr;
   p->seq_row0 = nullptr;
+  p->seg_info = nullptr;
   p->ev_start = nullptr;
   p->ev_stop = nullptr;
   const int64_t segments = static_cast<int64_t>(d.num_seqs) * d.num_kv_heads * p->col_blocks;
@@ -165,36 +173,42 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
     return hip_fail(e);
   }
   if (p->occupancy < 1) p->occupancy = 1;
+  // Units sharing the chunks: waves for the packed decode layout (each wave
+  // streams its own range), workgroups otherwise.
   const int64_t max_chunks = segments * ceil_div(d.max_ctx_len, kChunkTokens);
-  int64_t grid;
+  const int64_t per_unit_min = v.packed ? kMinChunksPerWave : kMinChunksPerGroup;
+  const int64_t unit_waves = v.packed ? 1 : pa::kWavesPerGroup;
+  int64_t units;
   if (d.num_kv_splits > 0) {
-    grid = segments * d.num_kv_splits;
+    units = segments * d.num_kv_splits;
   } else {
     // wide column tiles hold one workgroup per compute unit: queue several
     const int per_cu = v.col_tiles > 1 ? std::max(p->occupancy, 4) : p->occupancy;
-    grid = static_cast<int64_t>(p->num_cus) * per_cu;
-    grid = std::min<int64_t>(grid, std::max<int64_t>(1, max_chunks / kMinChunksPerGroup));
+    units = static_cast<int64_t>(p->num_cus) * per_cu * pa::kWavesPerGroup / unit_waves;
   }
-  grid = std::min<int64_t>(grid, max_chunks);
-  grid = std::max<int64_t>(grid, 1);
-  if (grid > 0x3fffffffLL) {
+  units = std::min<int64_t>(units, std::max<int64_t>(1, max_chunks / per_unit_min));
+  units = std::max<int64_t>(units, 1);
+  if (units > 0x3fffffffLL) {
     delete p;
     return ATTN_ERR_UNSUPPORTED;
   }
-  p->grid = static_cast<int>(grid);
+  p->max_units = static_cast<int>(units);
+  p->grid = static_cast<int>(ceil_div(units * unit_waves, pa::kWavesPerGroup));
   // merge: one workgroup per (segment, query column of its block)
-  p->merge_grid = p->grid > 1 ? p->num_segments * p->cols_per_block : 0;
+  p->merge_grid = units > 1 ? p->num_segments * p->cols_per_block : 0;
 
-  // Workspace, allocated once: partial slots (segments + grid of them, one
-  // per (segment, workgroup) pair that can occur), and where each sequence
+  // Workspace, allocated once: partial slots (segments + units of them, one
+  // per (segment, unit) pair that can occur), and where each sequence
   // starts in the chunk list.
-  const size_t slots = static_cast<size_t>(segments) + static_cast<size_t>(grid);
+  const size_t slots = static_cast<size_t>(segments) + static_cast<size_t>(units);
   const size_t o_bytes = slots * p->cols_per_block * d.head_dim * sizeof(float);
   const size_t ml_bytes = slots * p->cols_per_block * 2 * sizeof(float);
   const size_t c0_bytes = (static_cast<size_t>(d.num_seqs) + 1) * sizeof(int64_t);
   const size_t r0_bytes = static_cast<size_t>(d.num_seqs) * sizeof(int32_t);
+  const size_t si_bytes = static_cast<size_t>(segments) * 2 * sizeof(int32_t);
   auto round_up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  p->workspace_bytes = round_up(o_bytes) + round_up(ml_bytes) + round_up(c0_bytes) + round_up(r0_bytes);
+  p->workspace_bytes =
+      round_up(o_bytes) + round_up(ml_bytes) + round_up(c0_bytes) + round_up(r0_bytes) + round_up(si_bytes);
   e = hipMalloc(&p->workspace, p->workspace_bytes);
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -209,6 +223,8 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   p->seq_chunk0 = reinterpret_cast<int64_t*>(ws);
   ws += round_up(c0_bytes);
   p->seq_row0 = reinterpret_cast<int32_t*>(ws);
+  ws += round_up(r0_bytes);
+  p->seg_info = reinterpret_cast<int2*>(ws);
   *out_plan = p;
   return ATTN_OK;
 }
@@ -234,6 +250,8 @@ attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info) {
   info->num_segments = plan->num_segments;
   info->grid_size = plan->grid;
   info->merge_grid_size = plan->merge_grid;
+  info->work_units = plan->max_units;
+  info->packed = plan->variant.packed ? 1 : 0;
   info->resident_groups_per_cu = plan->occupancy;
   info->compute_units = plan->num_cus;
   info->workspace_bytes = plan->workspace_bytes;
@@ -285,8 +303,11 @@ attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t*
   sp.max_q_len = d.max_q_len;
   sp.cols_per_block = plan->cols_per_block;
   sp.col_blocks = plan->col_blocks;
+  sp.wave_units = plan->variant.packed ? 1 : 0;
+  sp.max_units = plan->max_units;
   sp.seq_chunk0 = plan->seq_chunk0;
   sp.seq_row0 = plan->seq_row0;
+  sp.seg_info = plan->seg_info;
   sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
   sp.qk_scale_log2 = plan->sm_scale * 1.4426950408889634f;
 

@@ -24,9 +24,9 @@
 // the merge kernel combines them by log-sum-exp.
 //
 // Per chunk, in each wave (lane = 16*lq + ln):
-//   * K: lane reads 32 (D=128) contiguous bytes of token slot ln at
-//     d in [lq*D/4, (lq+1)*D/4) of both pages -- 16-byte loads, the whole
-//     2 KB (page, head) chunk covered once by the wave;
+//   * K: lane reads the bytes of token slot ln at d in [lq*D/4, (lq+1)*D/4)
+//     of both pages as 16-byte loads; in the (page, head) layout each load
+//     instruction of the wave reads whole 128-byte lines (1 KB per load);
 //   * S^T = K * Q^T with v_mfma_f32_16x16x32_bf16: A = K (rows = 16 keys of
 //     a page, exact FP8->bf16), B = Q^T (columns = query columns).  The
 //     d-order inside the contraction is permuted identically on both sides;
@@ -37,7 +37,8 @@
 //     exact to ~2^-17 relative), so PV adds no rounding beyond fp32;
 //   * O^T += V^T * P~^T: A = V^T (rows = d, k = the 32 keys), B = P~^T taken
 //     straight from the S^T accumulator layout.  The 4-token interleave of
-//     the V page layout makes each lane's operand 32 contiguous bytes.
+//     the V page layout gives each lane its operand in 16-byte loads that,
+//     across the wave, read whole lines.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -220,10 +221,62 @@ __device__ void write_seq_meta(const StreamParams& p, int lane) {
   if (lane == 0) p.seq_chunk0[p.num_seqs] = carry;
 }
 
-// First workgroup whose range holds global chunk g: ranges start at
+// Units that share the chunks: waves when each wave streams its own range
+// (packed decode; at least kMinChunksPerWave chunks each, so small problems
+// stay in one wave), workgroups otherwise.
+constexpr int kMinChunksPerWave = 8;
+
+__device__ __forceinline__ int work_units(const StreamParams& p, int64_t T, int grid) {
+  if (!p.wave_units) return grid;
+  const int64_t want = T / kMinChunksPerWave;
+  return (int)(want < 1 ? 1 : (want < p.max_units ? want : p.max_units));
+}
+
+// First unit whose range holds global chunk g: ranges start at
 // floor(w T / W), so it is the largest w with w T < (g + 1) W.
 __device__ __forceinline__ int wg_of_chunk(int64_t g, int64_t T, int W) {
   return (int)(((g + 1) * (int64_t)W + T - 1) / T) - 1;
+}
+
+// ---- ring of register buffers ---------------------------------------------
+// Units k < nk of a wave go through NRING buffers: unit k lives in buffer
+// k % NRING and the buffer is refilled with unit k + NRING right after unit k
+// is consumed.  In the steady state every consumption is followed by a refill
+// unconditionally, so the compiler knows exactly how many loads were issued
+// after each buffer's and waits for that buffer alone (a conditional refill
+// would make it wait for every outstanding load).  issue(k, slot) and
+// step(k, slot) take the buffer index as a compile-time constant after
+// unrolling.
+template <int NRING, class Issue, class Step>
+__device__ __forceinline__ void ring_loop(int nk, Issue&& issue, Step&& step) {
+  if (nk >= NRING) {
+#pragma unroll
+    for (int j = 0; j < NRING; ++j) issue(j, j);
+    int k = 0;
+    for (; k + 2 * NRING <= nk; k += NRING) {
+#pragma unroll
+      for (int j = 0; j < NRING; ++j) {
+        step(k + j, j);
+        issue(k + j + NRING, j);
+      }
+    }
+    // NRING <= nk - k < 2 * NRING units remain
+#pragma unroll
+    for (int j = 0; j < NRING; ++j) {
+      step(k + j, j);
+      if (k + j + NRING < nk) issue(k + j + NRING, j);
+    }
+#pragma unroll
+    for (int j = 0; j < NRING; ++j)
+      if (k + NRING + j < nk) step(k + NRING + j, j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NRING; ++j)
+      if (j < nk) issue(j, j);
+#pragma unroll
+    for (int j = 0; j < NRING; ++j)
+      if (j < nk) step(j, j);
+  }
 }
 
 // ---- one piece of a segment ----------------------------------------------
@@ -310,8 +363,13 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
   }
 
   const int32_t* bt = p.block_table + (size_t)pc.b * p.bt_stride;
-  const uint32_t koff = k_in_chunk(ln, lq * GD::DQ, D);
-  const uint32_t voff = v_in_chunk(4 * lq, GD::NVB * ln, D);
+  // load i of a lane reads 16 bytes: K block d = lq*DQ + 16i of slot ln; V
+  // values d = NVB*ln + 4i .. +3 of the slots 4lq..4lq+3
+  uint32_t koff[GD::NKV], voff[GD::NVV];
+#pragma unroll
+  for (int i = 0; i < GD::NKV; ++i) koff[i] = k_in_chunk(ln, lq * GD::DQ + 16 * i, D);
+#pragma unroll
+  for (int i = 0; i < GD::NVV; ++i) voff[i] = v_in_chunk(4 * lq, GD::NVB * ln + 4 * i, D);
   const uint8_t* kpool = p.k_pages;
   const uint8_t* vpool = p.v_pages;
 
@@ -348,19 +406,23 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
   // fill ring slot j with chunk k (k < nk); a new batch of block-table
   // entries is fetched when k starts one (every chunk before k has already
   // been issued and has its scales latched)
-  auto issue = [&](int k, u32x4 (&kb)[2][GD::NKV], u32x4 (&vb)[2][GD::NVV], float (&skj)[2], float (&svj)[2]) {
+  auto issue = [&](int k, int j) {
+    u32x4 (&kb)[2][GD::NKV] = kbuf[j];
+    u32x4 (&vb)[2][GD::NVV] = vbuf[j];
+    float (&skj)[2] = skb[j];
+    float (&svj)[2] = svb[j];
     if ((k & 31) == 0) load_batch(k);
     const int slot = 2 * (k & 31);
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       const int32_t ph = __builtin_amdgcn_readlane(bt_v, slot + pg);
       const uint64_t base = chunk_offset(ph, h, p.num_kv_heads, D);
-      const u32x4* kp = reinterpret_cast<const u32x4*>(kpool + base + koff);
-      const u32x4* vp = reinterpret_cast<const u32x4*>(vpool + base + voff);
 #pragma unroll
-      for (int i = 0; i < GD::NKV; ++i) kb[pg][i] = __builtin_nontemporal_load(kp + i);
+      for (int i = 0; i < GD::NKV; ++i)
+        kb[pg][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + base + koff[i]));
 #pragma unroll
-      for (int i = 0; i < GD::NVV; ++i) vb[pg][i] = __builtin_nontemporal_load(vp + i);
+      for (int i = 0; i < GD::NVV; ++i)
+        vb[pg][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + base + voff[i]));
     }
     // the scales are read after the KV loads are issued: waiting for them
     // (they were fetched before) leaves the KV loads in flight
@@ -372,8 +434,11 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
   };
 
   // compute chunk k from its ring slot
-  auto step = [&](int k, const u32x4 (&kc)[2][GD::NKV], const u32x4 (&vc)[2][GD::NVV], const float (&skc)[2],
-                  const float (&svc)[2]) {
+  auto step = [&](int k, int j) {
+    const u32x4 (&kc)[2][GD::NKV] = kbuf[j];
+    const u32x4 (&vc)[2][GD::NVV] = vbuf[j];
+    const float (&skc)[2] = skb[j];
+    const float (&svc)[2] = svb[j];
     const int c = c_begin + wave + k * NW;
     // S^T = K Q^T for both pages
     f32x4 sacc[2][NCT];
@@ -489,19 +554,7 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
     }
   };
 
-#pragma unroll
-  for (int j = 0; j < NBUF; ++j)
-    if (j < nk) issue(j, kbuf[j], vbuf[j], skb[j], svb[j]);
-  for (int k0 = 0; k0 < nk; k0 += NBUF) {
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j) {
-      const int k = k0 + j;
-      if (k < nk) {
-        step(k, kbuf[j], vbuf[j], skb[j], svb[j]);
-        if (k + NBUF < nk) issue(k + NBUF, kbuf[j], vbuf[j], skb[j], svb[j]);
-      }
-    }
-  }
+  ring_loop<NBUF>(nk, issue, step);
 
   // ---- per-wave finish: column sums; fold spare-column low parts ----------
 #pragma unroll
@@ -608,22 +661,338 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
   }
 }
 
+// ---- packed decode piece: at most 4 query columns --------------------------
+// Four consecutive pages share one 16x16 score tile.  Each page has its own
+// QK accumulator (K of the page as A, the query columns replicated over the
+// 16 B columns), and lane (lq, ln) keeps the scores of page ln/4, keys
+// 4lq..4lq+3, query column ln%4: every lane then holds four useful scores and
+// the softmax runs on full registers.  The running max is lazy: it moves
+// only when a new score exceeds it by more than kLazyLog2 (weights stay
+// below 2^kLazyLog2, harmless in fp32 and in the bf16 hi + lo split), so the
+// accumulators are almost never rescaled.  In PV each chunk (two pages) uses
+// a B operand in which a lane's P sits in the half of its own page, so the
+// output column ln accumulates the pages at group position ln/4; the four
+// positions are summed at the end of the piece.  One wave streams the whole
+// piece in groups of two chunks (four pages, 64 keys); keys at or past the
+// piece's end (or L) are masked.
+constexpr float kLazyLog2 = 8.f;
+#ifndef PACKED_RING
+#define PACKED_RING 1
+#endif
+#ifndef PACKED_WAVES_PER_SIMD
+#define PACKED_WAVES_PER_SIMD 2
+#endif
+
+__device__ __forceinline__ float dpp_ror4(float x) {
+  return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x124 /*row_ror:4*/, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_ror8(float x) {
+  return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x128 /*row_ror:8*/, 0xf, 0xf, false));
+}
+
+template <int D, bool QF32, bool OUTF32, int NRING>
+__device__ __forceinline__ void run_piece_packed(const StreamParams& p, const PieceDesc& pc, int lane) {
+  using GD = Geo<D>;
+  constexpr int NP = QF32 ? 3 : 1;
+  const int lq = lane >> 4;
+  const int ln = lane & 15;
+  const int pj = ln >> 2;  // group position of the page whose scores this lane keeps
+  const int qc = ln & 3;   // query column of this lane
+  const int h = pc.h;
+  const int L = pc.L;
+  const int Qb = pc.Q;
+  const int G = p.group;
+  const int ncols = G * Qb;
+  const int col0 = pc.cb * p.cols_per_block;
+  const int cols_here = min(p.cols_per_block, ncols - col0);
+  const int npages = (L + kPageSize - 1) / kPageSize;
+  const int kend = min(L, pc.c_end * kChunk);  // keys past this belong to another piece
+  const int lim_lo = L - Qb + col0 / G;         // smallest causal limit of the block
+
+  // ---- Q operand: B column ln is query column qc ---------------------------
+  const bool qvalid = qc < cols_here;
+  const int gc = col0 + (qvalid ? qc : 0);
+  const int qi = gc / G;
+  const int qg = gc - qi * G;
+  const int lim = qvalid ? (L - Qb + qi) : -1;
+  const int qrow = pc.row0 + qi;
+  const int qhead = h * G + qg;
+  bf16x8 qop[NP][GD::NSLAB];
+  {
+    const size_t qoff = ((size_t)qrow * p.num_q_heads + qhead) * D + (size_t)lq * GD::DQ;
+    if constexpr (QF32) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(p.q) + qoff);
+#pragma unroll
+      for (int s = 0; s < GD::NSLAB; ++s) {
+        float x[8];
+        if (qvalid) {
+          const u32x4 w0 = src[2 * s], w1 = src[2 * s + 1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[j] = __uint_as_float(w0[j]);
+            x[4 + j] = __uint_as_float(w1[j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = 0.f;
+        }
+        split_q_f32(x, qop[0][s], qop[1][s], qop[2][s]);
+      }
+    } else {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) + qoff);
+#pragma unroll
+      for (int s = 0; s < GD::NSLAB; ++s) {
+        const u32x4 w = qvalid ? src[s] : u32x4{0u, 0u, 0u, 0u};
+        qop[0][s] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
+
+  f32x4 o[GD::NVB];
+#pragma unroll
+  for (int c = 0; c < GD::NVB; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf;  // reference max (log2 units), the same in the 16 lanes of a query column
+  float l = 0.f;      // this lane's share of the weight sum
+
+  const int32_t* bt = p.block_table + (size_t)pc.b * p.bt_stride;
+  // load i of a lane reads 16 bytes: K block d = lq*DQ + 16i of slot ln; V
+  // values d = NVB*ln + 4i .. +3 of the slots 4lq..4lq+3
+  uint32_t koff[GD::NKV], voff[GD::NVV];
+#pragma unroll
+  for (int i = 0; i < GD::NKV; ++i) koff[i] = k_in_chunk(ln, lq * GD::DQ + 16 * i, D);
+#pragma unroll
+  for (int i = 0; i < GD::NVV; ++i) voff[i] = v_in_chunk(4 * lq, GD::NVB * ln + 4 * i, D);
+  const uint8_t* kpool = p.k_pages;
+  const uint8_t* vpool = p.v_pages;
+
+  // The wave's groups start at chunk c_begin + 2k, k < nk (the last group of
+  // an odd piece has one chunk; its second is masked by kend).
+  const int c_begin = pc.c_begin;
+  const int nk = (pc.c_end - c_begin + 1) / 2;
+
+  // block-table batch: lane j holds the page of group k0 + j/4, position j%4,
+  // and that page's K and V scales
+  int32_t bt_v = 0;
+  float sk_v = 0.f, sv_v = 0.f;
+  auto load_batch = [&](int k0) {
+    const int k = k0 + (lane >> 2);
+    int32_t ph = 0;
+    float a = 0.f, bsc = 0.f;
+    if (k < nk) {
+      const int c = c_begin + 2 * k;
+      const int pg = min(2 * c + (lane & 3), npages - 1);  // missing pages repeat the last one
+      ph = bt[pg];
+      const int64_t sidx = (int64_t)ph * p.num_kv_heads + h;
+      a = p.kv_scales[sidx];
+      bsc = p.kv_scales[p.v_scale_offset + sidx];
+    }
+    bt_v = ph;
+    sk_v = a;
+    sv_v = bsc;
+  };
+
+  u32x4 kbuf[NRING][4][GD::NKV], vbuf[NRING][4][GD::NVV];
+  float skb[NRING], svb[NRING];  // scales of the page this lane's scores belong to
+  auto issue = [&](int k, int j) {
+    u32x4 (&kb)[4][GD::NKV] = kbuf[j];
+    u32x4 (&vb)[4][GD::NVV] = vbuf[j];
+    float& skl = skb[j];
+    float& svl = svb[j];
+    if ((k & 15) == 0) load_batch(k);
+    const int e = 4 * (k & 15);
+#pragma unroll
+    for (int pg = 0; pg < 4; ++pg) {
+      const int32_t ph = __builtin_amdgcn_readlane(bt_v, e + pg);
+      const uint64_t base = chunk_offset(ph, h, p.num_kv_heads, D);
+#pragma unroll
+      for (int i = 0; i < GD::NKV; ++i)
+        kb[pg][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + base + koff[i]));
+    }
+#pragma unroll
+    for (int pg = 0; pg < 4; ++pg) {
+      const int32_t ph = __builtin_amdgcn_readlane(bt_v, e + pg);
+      const uint64_t base = chunk_offset(ph, h, p.num_kv_heads, D);
+#pragma unroll
+      for (int i = 0; i < GD::NVV; ++i)
+        vb[pg][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + base + voff[i]));
+    }
+    skl = __shfl(sk_v, e + pj);
+    svl = __shfl(sv_v, e + pj);
+  };
+
+  auto step = [&](int k, int j) {
+    const u32x4 (&kc)[4][GD::NKV] = kbuf[j];
+    const u32x4 (&vc)[4][GD::NVV] = vbuf[j];
+    const float skl = skb[j];
+    const float svl = svb[j];
+    const int c = c_begin + 2 * k;
+    const int key0 = c * kChunk;  // first key of the group
+    // QK: one accumulator per page; each lane keeps the tile of its page
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pg = 0; pg < 4; ++pg) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < GD::NSLAB; ++s) {
+        const u32x4 w = kc[pg][(2 * s) / 4];
+        const bf16x8 kb = fp8x8_to_bf16x8(w[(2 * s) % 4], w[(2 * s) % 4 + 1]);
+#pragma unroll
+        for (int part = 0; part < NP; ++part)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[part][s], acc, 0, 0, 0);
+      }
+      if (pj == pg) sc = acc;
+    }
+    const float fk = p.qk_scale_log2 * skl;
+    const int kl = key0 + 16 * pj + 4 * lq;  // key of sc[0]
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = sc[i] * fk;
+    if (key0 + 2 * kChunk > kend || key0 + 2 * kChunk - 1 > lim_lo) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (kl + i <= lim && kl + i < kend) ? x[i] : kNegInf;
+    }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = max_over_lq(mx);
+    mx = fmaxf(mx, dpp_ror4(mx));
+    mx = fmaxf(mx, dpp_ror8(mx));
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazyLog2)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - ((mn == kNegInf) ? 0.f : mn));
+#pragma unroll
+      for (int cb2 = 0; cb2 < GD::NVB; ++cb2) o[cb2] *= alpha;
+      l *= alpha;
+      m = mn;
+    }
+    const float base = (m == kNegInf) ? 0.f : m;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(x[i] - base);
+      l += pr[i];
+    }
+    // P~ = p * V scale as bf16 hi + lo
+    float a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = pr[i] * svl;
+    const uint32_t hw0 = pack_bf16(a[0], a[1]);
+    const uint32_t hw1 = pack_bf16(a[2], a[3]);
+    const uint32_t lw0 = pack_bf16(a[0] - bf16_lo(hw0), a[1] - bf16_hi(hw0));
+    const uint32_t lw1 = pack_bf16(a[2] - bf16_lo(hw1), a[3] - bf16_hi(hw1));
+    // PV, one chunk (two pages) at a time
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      const uint32_t mA = (pj == 2 * ch) ? 0xffffffffu : 0u;
+      const uint32_t mB = (pj == 2 * ch + 1) ? 0xffffffffu : 0u;
+      const bf16x8 bhi = __builtin_bit_cast(bf16x8, u32x4{hw0 & mA, hw1 & mA, hw0 & mB, hw1 & mB});
+      const bf16x8 blo = __builtin_bit_cast(bf16x8, u32x4{lw0 & mA, lw1 & mA, lw0 & mB, lw1 & mB});
+      const int kc0 = key0 + ch * kChunk + 4 * lq;  // key of the lane's first V byte of page 2ch
+      uint32_t vm0 = 0xffffffffu, vm1 = 0xffffffffu;
+      if (key0 + ch * kChunk + kChunk > L) {  // bytes of keys >= L may be anything: select them to 0
+        vm0 = 0u;
+        vm1 = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vm0 |= (kc0 + j < L) ? (0xffu << (8 * j)) : 0u;
+          vm1 |= (kc0 + 16 + j < L) ? (0xffu << (8 * j)) : 0u;
+        }
+      }
+#pragma unroll
+      for (int cblk = 0; cblk < GD::NVB; ++cblk) {
+        const uint32_t w0 = vc[2 * ch][cblk / 4][cblk % 4] & vm0;
+        const uint32_t w1 = vc[2 * ch + 1][cblk / 4][cblk % 4] & vm1;
+        const bf16x8 va = fp8x8_to_bf16x8(w0, w1);
+        o[cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bhi, o[cblk], 0, 0, 0);
+        o[cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, blo, o[cblk], 0, 0, 0);
+      }
+    }
+  };
+
+  ring_loop<NRING>(nk, issue, step);
+
+  // ---- per-wave finish: sum over lane quarters and page positions ---------
+  l = sum_over_lq(l);
+  l += dpp_ror4(l);
+  l += dpp_ror8(l);
+#pragma unroll
+  for (int cblk = 0; cblk < GD::NVB; ++cblk)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = o[cblk][j];
+      v += dpp_ror4(v);
+      v += dpp_ror8(v);
+      o[cblk][j] = v;
+    }
+
+  // ---- write: final output, or this piece's partial -----------------------
+  if (pj == 0 && qc < cols_here) {
+    if (pc.whole) {
+      const float inv = 1.f / l;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const size_t off = ((size_t)qrow * p.num_q_heads + qhead) * D + (size_t)GD::NVB * (4 * lq + j);
+        if constexpr (OUTF32) {
+          float* dst = static_cast<float*>(p.out) + off;
+#pragma unroll
+          for (int c4 = 0; c4 < GD::NVB / 4; ++c4) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = o[4 * c4 + e][j] * inv;
+            *reinterpret_cast<f32x4*>(dst + 4 * c4) = v;
+          }
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(p.out) + off;
+          uint32_t w[GD::NVB / 2];
+#pragma unroll
+          for (int e = 0; e < GD::NVB / 2; ++e) w[e] = pack_bf16(o[2 * e][j] * inv, o[2 * e + 1][j] * inv);
+          if constexpr (GD::NVB == 8) {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+          } else {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+          }
+        }
+      }
+    } else {
+      float* po = p.part_o + ((size_t)pc.slot * p.cols_per_block + qc) * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float* dst = po + GD::NVB * (4 * lq + j);
+#pragma unroll
+        for (int c4 = 0; c4 < GD::NVB / 4; ++c4) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[4 * c4 + e][j];
+          *reinterpret_cast<f32x4*>(dst + 4 * c4) = v;
+        }
+      }
+      if (lq == 0) {
+        float* pm = p.part_ml + ((size_t)pc.slot * p.cols_per_block + qc) * 2;
+        pm[0] = m;
+        pm[1] = l;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // ---- attention kernel: one balanced chunk range per workgroup -------------
-// A single column tile is held to 256 registers per wave (two waves per
-// SIMD, eight per compute unit, each with three 8 KB chunks in flight);
-// wider tiles keep the whole register file for their accumulators.
+// NCT = 0 is the packed decode layout (at most 4 query columns), otherwise
+// NCT 16-column tiles.  Packed and single-tile variants are held to 256
+// registers per wave (two waves per SIMD, eight per compute unit, each with
+// 24-32 KB of K+V in flight); wider tiles keep the whole register file for
+// their accumulators.
 template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32>
-__global__ __launch_bounds__(64 * kWavesPerGroup, (NCT == 1 ? 2 : 1)) void attn_stream_kernel(StreamParams p) {
+__global__ __launch_bounds__(64 * kWavesPerGroup, (NCT == 0 ? PACKED_WAVES_PER_SIMD : NCT == 1 ? 2 : 1)) void attn_stream_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int w = blockIdx.x;
-  const int W = gridDim.x;
 
-  if (w == 0 && wave == 0) write_seq_meta(p, lane);
+  if (blockIdx.x == 0 && wave == 0) write_seq_meta(p, lane);
   const SeqLens c0 = load_seq(p, lane);
   const int64_t T = total_chunks(p, lane, c0);
+  // this unit's share of the chunks: a wave's (packed) or the workgroup's
+  const int W = work_units(p, T, gridDim.x);
+  const int w = (NCT == 0) ? (int)blockIdx.x * kWavesPerGroup + wave : (int)blockIdx.x;
+  if (w >= W) return;
   const int64_t lo = (int64_t)w * T / W;
   const int64_t hi = (int64_t)(w + 1) * T / W;
   if (lo >= hi) return;
@@ -659,10 +1028,23 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (NCT == 1 ? 2 : 1)) void attn_
     pc.c_begin = r;
     pc.c_end = r + take;
     pc.whole = (r == 0) && (take == n);
-    pc.slot = ((b * p.num_kv_heads + h) * p.col_blocks + cb) + w;
-    // ring depth: a single column tile leaves registers for three chunks in
-    // flight per wave, wider tiles for two
-    run_piece<D, NCT, DUPLO, QF32, OUTF32, (NCT == 1 ? 3 : 2)>(p, pc, lane, wave);
+    const int seg = (b * p.num_kv_heads + h) * p.col_blocks + cb;
+    pc.slot = seg + w;
+    if (r == 0 && lane == 0 && (NCT == 0 || wave == 0)) {
+      // this unit holds the segment's first chunk: tell the merge kernel
+      // where the segment's partials start and how many units hold pieces
+      const int last = pc.whole ? w : wg_of_chunk(cur + n - 1, T, W);
+      p.seg_info[seg] = make_int2(seg + w, last - w + 1);
+    }
+    if constexpr (NCT == 0) {
+      // at most 4 query columns: four pages per score tile, two groups of
+      // four pages (32 KB of K+V) in flight per wave
+      run_piece_packed<D, QF32, OUTF32, PACKED_RING>(p, pc, lane);
+    } else {
+      // ring depth: a single column tile leaves registers for three chunks
+      // in flight per wave, wider tiles for two
+      run_piece<D, (NCT == 0 ? 1 : NCT), DUPLO, QF32, OUTF32, (NCT == 1 ? 3 : 2)>(p, pc, lane, wave);
+    }
     cur += take;
     if (cur >= hi) break;
     // next non-empty segment
@@ -700,20 +1082,22 @@ __global__ __launch_bounds__(kMergeGroups * (D / 4)) void split_merge_kernel(Str
   const int cb = s % p.col_blocks;
   const int h = (s / p.col_blocks) % p.num_kv_heads;
   const int b = s / (p.col_blocks * p.num_kv_heads);
+  // independent loads, issued together: lengths (a segment without chunks in
+  // this forward has no fresh metadata), the segment's metadata, the total
   const int L = p.ctx_lens[b];
   const int Q = p.q_lens[b];
+  const int2 si = p.seg_info[s];
+  const int64_t T = p.seq_chunk0[p.num_seqs];
+  const int rows = p.seq_row0[b];
   const int n = seg_chunks(L, Q, p.group, p.cols_per_block, cb);
   const int G = p.group;
   const int col0 = cb * p.cols_per_block;
   if (n == 0 || col0 + rc >= G * Q) return;
-  const int64_t T = p.seq_chunk0[p.num_seqs];
-  int64_t g = p.seq_chunk0[b] + (int64_t)h * head_chunks(p, L, Q);
-  for (int c = 0; c < cb; ++c) g += seg_chunks(L, Q, G, p.cols_per_block, c);
-  const int w_first = wg_of_chunk(g, T, attn_grid);
-  const int w_last = wg_of_chunk(g + n - 1, T, attn_grid);
-  if (w_first == w_last) return;  // written whole by the attention kernel
-  const int nparts = w_last - w_first + 1;
-  const int slot0 = s + w_first;
+  const int nparts = si.y;
+  if (nparts <= 1) return;  // written whole by the attention kernel
+  const int slot0 = si.x;
+  const int U = work_units(p, T, attn_grid);
+  const int w_first = slot0 - s;
 
   const int grp = threadIdx.x / V4;
   const int d4 = (threadIdx.x - grp * V4) * 4;
@@ -722,10 +1106,12 @@ __global__ __launch_bounds__(kMergeGroups * (D / 4)) void split_merge_kernel(Str
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
   for (int k = grp; k < nparts; k += kMergeGroups) {
-    // with more workgroups than chunks some ranges are empty: such a
-    // workgroup wrote no partial
-    const int64_t wk = w_first + k;
-    if ((wk * T) / attn_grid == ((wk + 1) * T) / attn_grid) continue;
+    // with more units than chunks some ranges are empty: such a unit wrote
+    // no partial
+    if (T < U) {
+      const int64_t wk = w_first + k;
+      if ((wk * T) / U == ((wk + 1) * T) / U) continue;
+    }
     const size_t ri = (size_t)(slot0 + k) * p.cols_per_block + rc;
     const float mk = p.part_ml[ri * 2];
     const float lk = p.part_ml[ri * 2 + 1];
@@ -763,7 +1149,7 @@ __global__ __launch_bounds__(kMergeGroups * (D / 4)) void split_merge_kernel(Str
   const int gc = col0 + rc;
   const int i = gc / G;
   const int gg = gc - i * G;
-  const size_t off = ((size_t)(p.seq_row0[b] + i) * p.num_q_heads + h * G + gg) * D + d4;
+  const size_t off = ((size_t)(rows + i) * p.num_q_heads + h * G + gg) * D + d4;
   if constexpr (OUTF32) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = o * inv;
   } else {
@@ -785,6 +1171,7 @@ static const void* kernel_d(const Variant& v) {
 
 template <int D>
 static const void* kernel_tiles(const Variant& v) {
+  if (v.packed) return kernel_d<D, 0, false>(v);
   if (v.dup_lo) return kernel_d<D, 1, true>(v);
   switch (v.col_tiles) {
     case 1: return kernel_d<D, 1, false>(v);

@@ -22,15 +22,24 @@ __device__ __forceinline__ uint64_t chunk_offset(int32_t page, int head, int num
   return ((uint64_t)(uint32_t)page * (uint64_t)num_kv_heads + (uint64_t)head) * (uint64_t)(kPageSize * head_dim);
 }
 
-// K chunk: token-major, byte of (slot, d) at slot * D + d.
+// K chunk: 16-byte blocks of d, slot-major inside a block; the byte of
+// (slot, d) sits at ((d / 16) * 16 + slot) * 16 + d % 16.  Sixteen lanes
+// reading one 16-byte block each for slots 0..15 cover 256 contiguous bytes.
 __device__ __forceinline__ uint32_t k_in_chunk(int slot, int d, int head_dim) {
-  return (uint32_t)(slot * head_dim + d);
+  (void)head_dim;
+  return (uint32_t)((((d >> 4) * kPageSize + slot) << 4) + (d & 15));
 }
 
-// V chunk: four consecutive slots interleaved per d, byte of (slot, d) at
-// ((slot / 4) * D + d) * 4 + slot % 4.
+// V chunk: four consecutive slots interleaved per d.  With NVB = D / 16 and
+// d = NVB * a + 4 * i + e, the byte of (slot, d) sits at
+// ((((slot / 4) * (D / 64) + i) * 16 + a) * 4 + e) * 4 + slot % 4: a lane's
+// 16-byte load holds 4 values of d times the 4 slots of its group, and the
+// 16 lanes a = 0..15 read 256 contiguous bytes.
 __device__ __forceinline__ uint32_t v_in_chunk(int slot, int d, int head_dim) {
-  return (uint32_t)((((slot >> 2) * head_dim) + d) * 4 + (slot & 3));
+  const int nvb = head_dim >> 4;
+  const int a = d / nvb;
+  const int r = d - a * nvb;
+  return (uint32_t)((((((slot >> 2) * (head_dim >> 6) + (r >> 2)) * 16 + a) * 4 + (r & 3)) << 2) + (slot & 3));
 }
 
 // Two FP8 E4M3 bytes of `w` (bytes 0,1 or, with HI, bytes 2,3) -> two bf16,

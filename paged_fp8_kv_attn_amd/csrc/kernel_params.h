@@ -22,6 +22,8 @@ struct StreamParams {
   float* part_ml;              // [slots][cols_per_block][2] running max (log2 units), sum
   int64_t* seq_chunk0;         // [B + 1] first global chunk of each sequence; [B] = total
   int32_t* seq_row0;           // [B] first query row of each sequence
+  int2* seg_info;              // [segments] written by the unit holding a segment's first
+                               // chunk: (first partial slot, pieces; 1 = written whole)
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -30,12 +32,15 @@ struct StreamParams {
   int32_t max_q_len;
   int32_t cols_per_block;      // query columns (new token x head of a group) per workgroup
   int32_t col_blocks;          // column blocks of one (sequence, kv head)
+  int32_t wave_units;          // 1: each wave streams its own share (packed decode)
+  int32_t max_units;           // units sharing the chunks at most (waves or workgroups)
   int64_t v_scale_offset;      // P * Hkv: start of the V scales in kv_scales
   float qk_scale_log2;         // sm_scale * log2(e)
 };
 
 struct Variant {
   int head_dim;     // 64 or 128
+  bool packed;      // at most 4 query columns: four pages share a score tile
   int col_tiles;    // 1, 2 or 4 MFMA column tiles of 16
   bool dup_lo;      // low halves of P in spare columns (col_tiles == 1, <= 8 columns)
   bool q_f32;

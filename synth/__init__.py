@@ -6,5 +6,8 @@ from .workloads import (  # noqa: F401
     POISON_BYTE,
     Workload,
     custom_workload,
+    empty_pages,
+    k_to_layout,
     make_workload,
+    v_to_layout,
 )

@@ -24,10 +24,17 @@ round-to-nearest-even E4M3 of fp32(x / scale), saturated to +-448.  Slots past
 a sequence's length and every unreferenced page hold the NaN code 0x7F; the
 scales of unreferenced pages are NaN; unused block-table entries are -1.
 
-Memory layouts (the library's ABI):
-  k_pages   uint8 [P][Hkv][S][D]          token-major inside a (page, head)
-  v_pages   uint8 [P][Hkv][S/4][D][4]     four consecutive tokens interleaved
-                                          per d inside a (page, head)
+Memory layouts (the library's ABI; S = 16 slots, D a multiple of 64):
+  k_pages   uint8 [P][Hkv][D/16][S][16]   inside a (page, head): 16-byte blocks
+                                          of d, slot-major within a block; the
+                                          byte of (slot s, d) is
+                                          k[p][h][d/16][s][d%16]
+  v_pages   uint8 [P][Hkv][S/4][D/64][16][4][4]
+                                          inside a (page, head): four
+                                          consecutive slots interleaved per d;
+                                          with NVB = D/16, d = NVB*a + 4*i + e,
+                                          the byte of (slot s, d) is
+                                          v[p][h][s/4][i][a][e][s%4]
   kv_scales fp32  [2][P][Hkv]             [0] = K scale, [1] = V scale
   block_table int32 [B][max_pages_per_seq]
   q         [sum(q_lens)][Hq][D]          sequences concatenated in order
@@ -58,8 +65,8 @@ class Workload:
     q_lens: np.ndarray  # int32 [B]
     ctx_lens: np.ndarray  # int32 [B]; keys visible to the last query row, new tokens included
     block_table: np.ndarray  # int32 [B][max_pages_per_seq]
-    k_pages: np.ndarray  # uint8 [P][Hkv][S][D]
-    v_pages: np.ndarray  # uint8 [P][Hkv][S/4][D][4]
+    k_pages: np.ndarray  # uint8 [P][Hkv][D/16][S][16]
+    v_pages: np.ndarray  # uint8 [P][Hkv][S/4][D/64][16][4][4]
     kv_scales: np.ndarray  # float32 [2][P][Hkv]
     q: torch.Tensor  # CPU tensor [sum Q][Hq][D], float32 or bfloat16
     max_q_len: int
@@ -117,6 +124,30 @@ def _quantise_pages(x: np.ndarray, valid_slots: np.ndarray):
     codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     codes = np.where(slot_ok[:, None, :, None], codes, np.uint8(POISON_BYTE)).astype(np.uint8)
     return codes, scale
+
+
+def empty_pages(num_pages: int, num_kv_heads: int, head_dim: int):
+    """K and V pools in the ABI layouts, every byte the poison code."""
+    if head_dim % 64:
+        raise ValueError("head_dim must be a multiple of 64")
+    S = PAGE_SIZE
+    k = np.full((num_pages, num_kv_heads, head_dim // 16, S, 16), POISON_BYTE, dtype=np.uint8)
+    v = np.full((num_pages, num_kv_heads, S // 4, head_dim // 64, 16, 4, 4), POISON_BYTE, dtype=np.uint8)
+    return k, v
+
+
+def k_to_layout(codes: np.ndarray) -> np.ndarray:
+    """[N][Hkv][S][D] bytes -> [N][Hkv][D/16][S][16]."""
+    n, hkv, s, d = codes.shape
+    return np.ascontiguousarray(codes.reshape(n, hkv, s, d // 16, 16).transpose(0, 1, 3, 2, 4))
+
+
+def v_to_layout(codes: np.ndarray) -> np.ndarray:
+    """[N][Hkv][S][D] bytes -> [N][Hkv][S/4][D/64][16][4][4]."""
+    n, hkv, s, d = codes.shape
+    # slot = 4*g + r; d = (D/16)*a + 4*i + e
+    x = codes.reshape(n, hkv, s // 4, 4, 16, d // 64, 4)  # [n][h][g][r][a][i][e]
+    return np.ascontiguousarray(x.transpose(0, 1, 2, 5, 4, 6, 3))  # [n][h][g][i][a][e][r]
 
 
 def build_workload(
@@ -183,13 +214,11 @@ def build_workload(
     v_codes, v_scale = _quantise_pages(v_f, valid)
     del v_f
 
-    k_pages = np.full((num_pages, num_kv_heads, S, head_dim), POISON_BYTE, dtype=np.uint8)
-    v_pages = np.full((num_pages, num_kv_heads, S // 4, head_dim, 4), POISON_BYTE, dtype=np.uint8)
+    k_pages, v_pages = empty_pages(num_pages, num_kv_heads, head_dim)
     kv_scales = np.full((2, num_pages, num_kv_heads), np.nan, dtype=np.float32)
     used_phys = phys[:used]
-    k_pages[used_phys] = k_codes
-    # [N][Hkv][S][D] -> [N][Hkv][S/4][4][D] -> [N][Hkv][S/4][D][4]
-    v_pages[used_phys] = v_codes.reshape(used, num_kv_heads, S // 4, 4, head_dim).transpose(0, 1, 2, 4, 3)
+    k_pages[used_phys] = k_to_layout(k_codes)
+    v_pages[used_phys] = v_to_layout(v_codes)
     kv_scales[0, used_phys] = k_scale
     kv_scales[1, used_phys] = v_scale
 

@@ -73,7 +73,7 @@ def brute_force_attention(w) -> np.ndarray:
                     s = t % S
                     acc = 0.0
                     for d in range(D):
-                        kb = kflat[((p * Hkv + h) * S + s) * D + d]
+                        kb = kflat[(((p * Hkv + h) * (D // 16) + d // 16) * S + s) * 16 + d % 16]
                         acc += float(q[row + i, hq, d]) * dec[kb] * ksc[p * Hkv + h]
                     zs.append(acc * scale)
                 zmax = max(zs)
@@ -84,7 +84,10 @@ def brute_force_attention(w) -> np.ndarray:
                     for t in range(position + 1):
                         p = int(w.block_table[b][t // S])
                         s = t % S
-                        vb = vflat[(((p * Hkv + h) * (S // 4) + s // 4) * D + d) * 4 + s % 4]
+                        nvb = D // 16
+                        va, vi, ve = d // nvb, (d % nvb) // 4, d % 4
+                        vb = vflat[(((((p * Hkv + h) * (S // 4) + s // 4) * (D // 64) + vi) * 16 + va) * 4 + ve) * 4
+                                   + s % 4]
                         acc += ws[t] * dec[vb] * vsc[p * Hkv + h]
                     out[row + i, hq, d] = acc / tot
         row += Q

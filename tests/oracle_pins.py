@@ -73,9 +73,9 @@ def pin_table_structure():
 
 def _tiny_cases():
     return [
-        custom_workload([1, 3, 2], [1, 20, 33], num_q_heads=4, num_kv_heads=2, head_dim=8, seed=11),
-        custom_workload([2], [17], num_q_heads=3, num_kv_heads=1, head_dim=8, seed=12, q_dtype="f32"),
-        custom_workload([1, 1], [16, 40], num_q_heads=6, num_kv_heads=3, head_dim=4, seed=13),
+        custom_workload([1, 3, 2], [1, 20, 33], num_q_heads=4, num_kv_heads=2, head_dim=64, seed=11),
+        custom_workload([2], [17], num_q_heads=3, num_kv_heads=1, head_dim=64, seed=12, q_dtype="f32"),
+        custom_workload([1, 1], [16, 40], num_q_heads=6, num_kv_heads=3, head_dim=64, seed=13),
     ]
 
 
@@ -105,7 +105,7 @@ def pin_sdpa():
 
 def pin_single_key():
     # one key: softmax weight 1, out = V~[0] for every head of the group
-    w = custom_workload([1, 1], [1, 1], num_q_heads=4, num_kv_heads=2, head_dim=16, seed=31)
+    w = custom_workload([1, 1], [1, 1], num_q_heads=4, num_kv_heads=2, head_dim=64, seed=31)
     got = _oracle(w)
     for b in range(2):
         lg = w.logical[b]
@@ -118,7 +118,7 @@ def pin_single_key():
 def pin_zero_keys_mean_of_visible():
     # K bytes all zero -> every visible key has score 0 -> out = mean of the
     # visible V~ rows; pins the causal limit and the per-sequence length.
-    w = custom_workload([3, 1, 4], [7, 18, 21], num_q_heads=4, num_kv_heads=2, head_dim=16, seed=32)
+    w = custom_workload([3, 1, 4], [7, 18, 21], num_q_heads=4, num_kv_heads=2, head_dim=64, seed=32)
     used = np.unique(w.block_table[w.block_table >= 0])
     w.k_pages[used] = 0
     got = _oracle(w)
@@ -137,7 +137,7 @@ def pin_zero_keys_mean_of_visible():
 
 def pin_constant_v():
     # every visible V~ equal -> out equals it whatever the weights
-    w = custom_workload([2, 1], [19, 40], num_q_heads=6, num_kv_heads=2, head_dim=8, seed=33)
+    w = custom_workload([2, 1], [19, 40], num_q_heads=6, num_kv_heads=2, head_dim=64, seed=33)
     used = np.unique(w.block_table[w.block_table >= 0])
     w.v_pages[used] = 0x44  # 3.0
     w.kv_scales[1][used] = 0.25
@@ -148,7 +148,7 @@ def pin_constant_v():
 def pin_scale_changes_result():
     # sm_scale is honoured: with 1/sqrt(D) replaced the result moves, and a
     # tiny explicit scale tends to the uniform mean (brute force agrees).
-    w = custom_workload([1], [30], num_q_heads=2, num_kv_heads=1, head_dim=8, seed=34)
+    w = custom_workload([1], [30], num_q_heads=2, num_kv_heads=1, head_dim=64, seed=34)
     w.sm_scale = 1e-9
     got = _oracle(w)
     lg = w.logical[0]

@@ -57,8 +57,8 @@ def test_poison_does_not_leak():
         L = int(w.ctx_lens[b])
         last = int(w.block_table[b][(L - 1) // 16])
         for s in range(L % 16 or 16, 16):
-            w.k_pages[last, :, s, :] = 0x7F
-            w.v_pages[last, :, s // 4, :, s % 4] = 0xFF
+            w.k_pages[last, :, :, s, :] = 0x7F
+            w.v_pages[last, :, s // 4, :, :, :, s % 4] = 0xFF
         w.block_table[b, (L + 15) // 16:] = 0x7FFFFFFF
     assert np.array_equal(run_gpu(w), ref)
 

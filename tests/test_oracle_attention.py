@@ -70,15 +70,15 @@ def test_poison_independence():
         L = int(w.ctx_lens[b])
         last = int(w.block_table[b][(L - 1) // 16])
         for s in range(L % 16 or 16, 16):
-            w.k_pages[last, :, s, :] = 0x7F
-            w.v_pages[last, :, s // 4, :, s % 4] = 0xFF
+            w.k_pages[last, :, :, s, :] = 0x7F
+            w.v_pages[last, :, s // 4, :, :, :, s % 4] = 0xFF
     np.testing.assert_array_equal(_run(w), ref)
 
 
 def test_shared_prefix_pages():
     # two sequences whose block tables point at the same physical pages and
     # whose query rows are equal produce equal outputs
-    w = custom_workload([1, 1], [40, 40], num_q_heads=4, num_kv_heads=2, head_dim=16, seed=43)
+    w = custom_workload([1, 1], [40, 40], num_q_heads=4, num_kv_heads=2, head_dim=64, seed=43)
     w.block_table[1] = w.block_table[0]
     w.q[1] = w.q[0]
     got = _run(w)
@@ -106,21 +106,26 @@ def test_named_workloads_reduced_vs_sdpa(name):
 def test_gather_round_trip():
     # logical bytes scattered by hand into a permuted pool come back unchanged
     rng = np.random.default_rng(45)
-    P, Hkv, S, D = 12, 2, 16, 8
+    P, Hkv, S, D = 12, 2, 16, 128
     L = 70
     logical_k = rng.integers(0, 256, (Hkv, L, D), dtype=np.uint8)
     logical_v = rng.integers(0, 256, (Hkv, L, D), dtype=np.uint8)
     phys = rng.permutation(P)[: (L + S - 1) // S]
-    k_pages = np.zeros((P, Hkv, S, D), np.uint8)
+    # written byte by byte at the flat offsets of the ABI layouts
+    k_flat = np.zeros(P * Hkv * S * D, np.uint8)
     v_flat = np.zeros(P * Hkv * S * D, np.uint8)
     scales = rng.standard_normal((2, P, Hkv)).astype(np.float32)
+    nvb = D // 16
     for t in range(L):
         p, s = phys[t // S], t % S
         for h in range(Hkv):
-            k_pages[p, h, s, :] = logical_k[h, t]
             for d in range(D):
-                v_flat[(((p * Hkv + h) * (S // 4) + s // 4) * D + d) * 4 + s % 4] = logical_v[h, t, d]
-    v_pages = v_flat.reshape(P, Hkv, S // 4, D, 4)
+                k_flat[(((p * Hkv + h) * (D // 16) + d // 16) * S + s) * 16 + d % 16] = logical_k[h, t, d]
+                a, i, e = d // nvb, (d % nvb) // 4, d % 4
+                v_flat[(((((p * Hkv + h) * (S // 4) + s // 4) * (D // 64) + i) * 16 + a) * 4 + e) * 4 + s % 4] = \
+                    logical_v[h, t, d]
+    k_pages = k_flat.reshape(P, Hkv, D // 16, S, 16)
+    v_pages = v_flat.reshape(P, Hkv, S // 4, D // 64, 16, 4, 4)
     bt = np.full(8, -1, np.int32)
     bt[: phys.size] = phys
     g = oracle.gather_sequence(k_pages, v_pages, scales, bt, L)

@@ -38,10 +38,22 @@ MUTATIONS = {
     "causal_off_by_one_high": ("last_visible_key", lambda L, Q, i: min(L - Q + i + 1, L - 1)),
     "no_causal_mask": ("last_visible_key", lambda L, Q, i: L - 1),
     "slot_shift": ("token_location", lambda row, t, S: (row[t // S], (t + 1) % S)),
+    # V read as if it had K's layout
     "v_read_with_k_layout": ("v_token_bytes",
-                             lambda v, pages, h, slots: v.reshape(v.shape[0], v.shape[1], -1, v.shape[3])[pages, h, slots, :]),
-    "v_interleave_swapped": ("v_token_bytes", lambda v, pages, h, slots: v[pages, h, slots % 4, :, slots // 4]),
-    "k_d_reversed": ("k_token_bytes", lambda k, pages, h, slots: k[pages, h, slots, ::-1]),
+                             lambda v, pages, h, slots: v.reshape(v.shape[0], v.shape[1], -1, 16, 16)
+                             [pages, h, :, slots, :].reshape(len(slots), -1)),
+    # the two slot digits of the 4-slot interleave exchanged
+    "v_interleave_swapped": ("v_token_bytes",
+                             lambda v, pages, h, slots: v[pages, h, slots % 4, :, :, :, slots // 4]
+                             .transpose(0, 2, 1, 3).reshape(len(slots), -1)),
+    # d taken in (i, a, e) order instead of (a, i, e)
+    "v_d_order_wrong": ("v_token_bytes",
+                        lambda v, pages, h, slots: v[pages, h, slots // 4, :, :, :, slots % 4].reshape(len(slots), -1)),
+    "k_d_reversed": ("k_token_bytes",
+                     lambda k, pages, h, slots: k[pages, h, :, slots, :].reshape(len(slots), -1)[:, ::-1]),
+    # K read token-major, as [S][D] inside a (page, head)
+    "k_token_major": ("k_token_bytes",
+                      lambda k, pages, h, slots: k.reshape(k.shape[0], k.shape[1], 16, -1)[pages, h, slots, :]),
     "scale_1_over_d": ("softmax_scale", lambda d, s: 1.0 / d if not s else s),
 }
 

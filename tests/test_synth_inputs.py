@@ -53,19 +53,25 @@ def test_pool_structure_and_poison():
     unused = np.setdiff1d(np.arange(w.num_pages), used)
     assert np.all(w.k_pages[unused] == POISON_BYTE) and np.all(np.isnan(w.kv_scales[:, unused]))
     last = w.block_table[0, npages[0] - 1]  # seq 0 has 17 tokens -> 1 valid slot in page 2
-    assert np.all(w.k_pages[last, :, 1:] == POISON_BYTE)
-    assert np.all(w.v_pages[last, :, 0, :, 1:] == POISON_BYTE)
+    assert np.all(w.k_pages[last, :, :, 1:] == POISON_BYTE)
+    assert np.all(w.v_pages[last, :, 0, :, :, :, 1:] == POISON_BYTE)
     assert np.all(w.v_pages[last, :, 1:] == POISON_BYTE)
+    assert not np.any(w.k_pages[last, :, :, 0] == POISON_BYTE)
 
 
 def test_logical_copy_matches_pool():
-    w = custom_workload([1, 1], [33, 16], num_q_heads=2, num_kv_heads=2, head_dim=8, seed=4)
+    w = custom_workload([1, 1], [33, 16], num_q_heads=2, num_kv_heads=2, head_dim=64, seed=4)
     for b in range(2):
         lg = w.logical[b]
         for t in range(int(w.ctx_lens[b])):
             p, s = w.block_table[b, t // 16], t % 16
-            np.testing.assert_array_equal(lg["k_bytes"][:, t], w.k_pages[p, :, s])
-            np.testing.assert_array_equal(lg["v_bytes"][:, t], w.v_pages[p, :, s // 4, :, s % 4])
+            D = w.head_dim
+            for d in (0, 1, 5, 15, 16, 17, 33, D - 1):
+                # flat-offset reading of the ABI layouts
+                np.testing.assert_array_equal(lg["k_bytes"][:, t, d], w.k_pages[p, :, d // 16, s, d % 16])
+                nvb = D // 16
+                np.testing.assert_array_equal(lg["v_bytes"][:, t, d],
+                                              w.v_pages[p, :, s // 4, (d % nvb) // 4, d // nvb, d % 4, s % 4])
             np.testing.assert_array_equal(lg["k_scale"][:, t], w.kv_scales[0, p])
 
 
