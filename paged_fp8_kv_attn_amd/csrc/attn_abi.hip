@@ -177,14 +177,15 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   // streams its own range), workgroups otherwise.
   const int64_t max_chunks = segments * ceil_div(d.max_ctx_len, kChunkTokens);
   const int64_t per_unit_min = v.packed ? kMinChunksPerWave : kMinChunksPerGroup;
-  const int64_t unit_waves = v.packed ? 1 : pa::kWavesPerGroup;
+  const int64_t wpg = pa::waves_per_group(v);
+  const int64_t unit_waves = v.packed ? 1 : wpg;
   int64_t units;
   if (d.num_kv_splits > 0) {
     units = segments * d.num_kv_splits;
   } else {
     // wide column tiles hold one workgroup per compute unit: queue several
     const int per_cu = v.col_tiles > 1 ? std::max(p->occupancy, 4) : p->occupancy;
-    units = static_cast<int64_t>(p->num_cus) * per_cu * pa::kWavesPerGroup / unit_waves;
+    units = static_cast<int64_t>(p->num_cus) * per_cu * wpg / unit_waves;
   }
   units = std::min<int64_t>(units, std::max<int64_t>(1, max_chunks / per_unit_min));
   units = std::max<int64_t>(units, 1);
@@ -193,7 +194,7 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
     return ATTN_ERR_UNSUPPORTED;
   }
   p->max_units = static_cast<int>(units);
-  p->grid = static_cast<int>(ceil_div(units * unit_waves, pa::kWavesPerGroup));
+  p->grid = static_cast<int>(ceil_div(units * unit_waves, wpg));
   // merge: one workgroup per (segment, query column of its block)
   p->merge_grid = units > 1 ? p->num_segments * p->cols_per_block : 0;
 
@@ -246,7 +247,7 @@ attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info) {
   info->dup_lo_columns = plan->variant.dup_lo ? 1 : 0;
   info->cols_per_block = plan->cols_per_block;
   info->col_blocks = plan->col_blocks;
-  info->waves_per_group = pa::kWavesPerGroup;
+  info->waves_per_group = pa::waves_per_group(plan->variant);
   info->num_segments = plan->num_segments;
   info->grid_size = plan->grid;
   info->merge_grid_size = plan->merge_grid;

@@ -676,6 +676,10 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
 // piece in groups of two chunks (four pages, 64 keys); keys at or past the
 // piece's end (or L) are masked.
 constexpr float kLazyLog2 = 8.f;
+// Packed decode tuning, measured on MI355X: one group of four pages (16 KB
+// of K+V) in flight per wave and two waves per SIMD.  Deeper rings (or one
+// wave per SIMD with a deeper ring) overfill the memory queues: latency grows,
+// bandwidth does not, and the slowest waves finish later.
 #ifndef PACKED_RING
 #define PACKED_RING 1
 #endif
@@ -982,7 +986,8 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
 // 24-32 KB of K+V in flight); wider tiles keep the whole register file for
 // their accumulators.
 template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32>
-__global__ __launch_bounds__(64 * kWavesPerGroup, (NCT == 0 ? PACKED_WAVES_PER_SIMD : NCT == 1 ? 2 : 1)) void attn_stream_kernel(StreamParams p) {
+__global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
+                             (NCT == 0 ? PACKED_WAVES_PER_SIMD : NCT == 1 ? 2 : 1)) void attn_stream_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -991,7 +996,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (NCT == 0 ? PACKED_WAVES_PER_S
   const int64_t T = total_chunks(p, lane, c0);
   // this unit's share of the chunks: a wave's (packed) or the workgroup's
   const int W = work_units(p, T, gridDim.x);
-  const int w = (NCT == 0) ? (int)blockIdx.x * kWavesPerGroup + wave : (int)blockIdx.x;
+  const int w = (NCT == 0) ? (int)blockIdx.x * kPackedWaves + wave : (int)blockIdx.x;
   if (w >= W) return;
   const int64_t lo = (int64_t)w * T / W;
   const int64_t hi = (int64_t)(w + 1) * T / W;
@@ -1037,8 +1042,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (NCT == 0 ? PACKED_WAVES_PER_S
       p.seg_info[seg] = make_int2(seg + w, last - w + 1);
     }
     if constexpr (NCT == 0) {
-      // at most 4 query columns: four pages per score tile, two groups of
-      // four pages (32 KB of K+V) in flight per wave
+      // at most 4 query columns: four pages per score tile
       run_piece_packed<D, QF32, OUTF32, PACKED_RING>(p, pc, lane);
     } else {
       // ring depth: a single column tile leaves registers for three chunks
@@ -1190,7 +1194,7 @@ static const void* stream_kernel(const Variant& v) {
 hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu) {
   const void* f = stream_kernel(v);
   if (!f) return hipErrorInvalidValue;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, 64 * kWavesPerGroup, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, 64 * waves_per_group(v), 0);
 }
 
 hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream,
@@ -1201,9 +1205,9 @@ hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int 
   void* args[] = {const_cast<StreamParams*>(&p)};
   if (ev_start) {
     // the events take the timestamps of this kernel's own dispatch
-    return hipExtLaunchKernel(f, dim3(grid), dim3(64 * kWavesPerGroup), args, 0, stream, ev_start, ev_stop, 0);
+    return hipExtLaunchKernel(f, dim3(grid), dim3(64 * waves_per_group(v)), args, 0, stream, ev_start, ev_stop, 0);
   }
-  return hipLaunchKernel(f, dim3(grid), dim3(64 * kWavesPerGroup), args, 0, stream);
+  return hipLaunchKernel(f, dim3(grid), dim3(64 * waves_per_group(v)), args, 0, stream);
 }
 
 hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, int attn_grid, hipStream_t stream) {

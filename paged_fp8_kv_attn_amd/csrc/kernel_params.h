@@ -48,10 +48,19 @@ struct Variant {
 };
 
 constexpr int kWavesPerGroup = 4;
+#ifndef PACKED_GROUP_WAVES
+#define PACKED_GROUP_WAVES 4
+#endif
+// Waves per workgroup of the packed decode kernel (each wave streams its own
+// chunk range, so the workgroup is only a unit of dispatch).
+constexpr int kPackedWaves = PACKED_GROUP_WAVES;
+
 
 // Attention kernel: `grid` workgroups share the key chunks of all segments
 // equally.  Partial slots needed: segments + grid.
 // With ev_start/ev_stop non-null they record the kernel's own start and end.
+inline int waves_per_group(const Variant& v) { return v.packed ? kPackedWaves : kWavesPerGroup; }
+
 hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream,
                                    hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // Resident workgroups per compute unit for the variant's attention kernel.
