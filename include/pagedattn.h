@@ -115,18 +115,24 @@ typedef struct {
  * shared equally by the work units of the attention kernel (its waves in the
  * packed layout, its workgroups otherwise). */
 typedef struct {
-  int32_t col_tiles;              /* 16-column MFMA tiles per workgroup (1, 2 or 4) */
+  int32_t col_tiles;              /* 16-column MFMA tiles per wave (1 or 2) */
   int32_t dup_lo_columns;         /* 1: low parts of P ride in spare MFMA columns */
   int32_t cols_per_block;         /* query columns (token x head of a group) per segment */
   int32_t col_blocks;             /* segments along the query columns of a group */
   int32_t waves_per_group;        /* waves per workgroup */
   int32_t num_segments;           /* B * Hkv * col_blocks */
   int32_t grid_size;              /* workgroups of the attention kernel */
-  int32_t merge_grid_size;        /* workgroups of the merge kernel (0: not launched) */
+  int32_t merge_grid_size;        /* merge kernel workgroups along x, one per segment
+                                     (0: not launched); along y one per column for
+                                     blocks of at most 4 columns, else one per
+                                     1024 / head_dim columns */
   int32_t work_units;             /* units sharing the chunks at most: waves when packed,
                                      workgroups otherwise */
   int32_t packed;                 /* 1: at most 4 query columns, four pages per score tile,
                                      one wave per chunk range */
+  int32_t shared_kv;              /* 1: more than 16 query columns; the waves of a
+                                     workgroup split the columns and share each KV
+                                     chunk through LDS */
   int32_t resident_groups_per_cu; /* attention workgroups one compute unit holds at once */
   int32_t compute_units;          /* of the plan's device */
   size_t workspace_bytes;         /* device bytes owned by the plan */

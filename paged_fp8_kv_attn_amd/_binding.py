@@ -72,6 +72,7 @@ class PlanInfo(ctypes.Structure):
         ("merge_grid_size", ctypes.c_int32),
         ("work_units", ctypes.c_int32),
         ("packed", ctypes.c_int32),
+        ("shared_kv", ctypes.c_int32),
         ("resident_groups_per_cu", ctypes.c_int32),
         ("compute_units", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),

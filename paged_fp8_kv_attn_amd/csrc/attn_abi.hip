@@ -30,6 +30,7 @@ struct attn_plan_s {
   int num_segments;  // (sequence, kv head, column block) units
   int grid;          // attention workgroups
   int max_units;     // waves (packed) or workgroups sharing the key chunks
+  int unit_min_chunks;  // chunks per unit at least (within [1, max_units] units)
   int occupancy;     // resident attention workgroups per compute unit
   int num_cus;
   float sm_scale;
@@ -37,9 +38,8 @@ struct attn_plan_s {
   size_t workspace_bytes;
   float* part_o;
   float* part_ml;
-  int64_t* seq_chunk0;
   int32_t* seq_row0;
-  int2* seg_info;
+  int2* seg_merge;
   int merge_grid;
   hipEvent_t ev_start;  // optional: recorded around the attention kernel
   hipEvent_t ev_stop;
@@ -60,7 +60,11 @@ int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
 constexpr int kChunkTokens = 32;  // keys per chunk (two pages)
 constexpr int kMinChunksPerGroup = 16;  // a workgroup's share is at least 4 chunks per wave
-constexpr int kMinChunksPerWave = 8;    // a wave's share in the packed layout (matches the kernel)
+constexpr int kMinChunksPerWave = 8;    // a wave's share in the packed layout
+// A shared-KV workgroup's share: wide column blocks write large partials
+// (columns x D fp32), so a unit streams at least 32 chunks (256 KB of K+V
+// at D = 128) per piece boundary it may cut.
+constexpr int kMinChunksPerTile = 32;
 
 attn_status_t validate_desc(const attn_plan_desc_t& d) {
   for (int r : d.reserved)
@@ -127,12 +131,18 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   } else if (cols <= 16) {
     v.col_tiles = 1;
     p->cols_per_block = 16;
-  } else if (cols <= 32) {
-    v.col_tiles = 2;
+  } else if (cols <= 32) {  // two waves share each KV chunk, one tile each
+    v.tile_waves = 2;
+    v.col_tiles = 1;
     p->cols_per_block = 32;
-  } else {
-    v.col_tiles = 4;
+  } else if (cols <= 64) {  // four waves, one tile each
+    v.tile_waves = 4;
+    v.col_tiles = 1;
     p->cols_per_block = 64;
+  } else {  // four waves, two tiles each: 128-column blocks
+    v.tile_waves = 4;
+    v.col_tiles = 2;
+    p->cols_per_block = 128;
   }
   p->col_blocks = ceil_div(cols, p->cols_per_block);
   p->variant = v;
@@ -142,9 +152,8 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   p->workspace_bytes = 0;
   p->part_o = nullptr;
   p->part_ml = nullptr;
-  p->seq_chunk0 = nullptr;
   p->seq_row0 = nullptr;
-  p->seg_info = nullptr;
+  p->seg_merge = nullptr;
   p->ev_start = nullptr;
   p->ev_stop = nullptr;
   const int64_t segments = static_cast<int64_t>(d.num_seqs) * d.num_kv_heads * p->col_blocks;
@@ -174,20 +183,23 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   }
   if (p->occupancy < 1) p->occupancy = 1;
   // Units sharing the chunks: waves for the packed decode layout (each wave
-  // streams its own range), workgroups otherwise.
+  // streams its own range), workgroups otherwise.  By default as many as
+  // the GPU keeps resident at once, so that every unit streams an equal
+  // share in a single round; the kernel uses one per unit_min_chunks chunks
+  // of the actual lengths, at most that many.
   const int64_t max_chunks = segments * ceil_div(d.max_ctx_len, kChunkTokens);
-  const int64_t per_unit_min = v.packed ? kMinChunksPerWave : kMinChunksPerGroup;
   const int64_t wpg = pa::waves_per_group(v);
   const int64_t unit_waves = v.packed ? 1 : wpg;
   int64_t units;
   if (d.num_kv_splits > 0) {
+    // forced: segments * n units, cut no finer than one chunk each
     units = segments * d.num_kv_splits;
+    p->unit_min_chunks = 1;
   } else {
-    // wide column tiles hold one workgroup per compute unit: queue several
-    const int per_cu = v.col_tiles > 1 ? std::max(p->occupancy, 4) : p->occupancy;
-    units = static_cast<int64_t>(p->num_cus) * per_cu * wpg / unit_waves;
+    units = static_cast<int64_t>(p->num_cus) * p->occupancy * wpg / unit_waves;
+    p->unit_min_chunks = v.packed ? kMinChunksPerWave : v.tile_waves > 0 ? kMinChunksPerTile : kMinChunksPerGroup;
   }
-  units = std::min<int64_t>(units, std::max<int64_t>(1, max_chunks / per_unit_min));
+  units = std::min<int64_t>(units, std::max<int64_t>(1, max_chunks / p->unit_min_chunks));
   units = std::max<int64_t>(units, 1);
   if (units > 0x3fffffffLL) {
     delete p;
@@ -195,21 +207,19 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   }
   p->max_units = static_cast<int>(units);
   p->grid = static_cast<int>(ceil_div(units * unit_waves, wpg));
-  // merge: one workgroup per (segment, query column of its block)
-  p->merge_grid = units > 1 ? p->num_segments * p->cols_per_block : 0;
+  // merge: one workgroup per segment (and slice of its columns)
+  p->merge_grid = units > 1 ? p->num_segments : 0;
 
   // Workspace, allocated once: partial slots (segments + units of them, one
-  // per (segment, unit) pair that can occur), and where each sequence
-  // starts in the chunk list.
+  // per (segment, unit) pair that can occur), each sequence's first query
+  // row, and each segment's partial slots.
   const size_t slots = static_cast<size_t>(segments) + static_cast<size_t>(units);
   const size_t o_bytes = slots * p->cols_per_block * d.head_dim * sizeof(float);
   const size_t ml_bytes = slots * p->cols_per_block * 2 * sizeof(float);
-  const size_t c0_bytes = (static_cast<size_t>(d.num_seqs) + 1) * sizeof(int64_t);
   const size_t r0_bytes = static_cast<size_t>(d.num_seqs) * sizeof(int32_t);
-  const size_t si_bytes = static_cast<size_t>(segments) * 2 * sizeof(int32_t);
+  const size_t job_bytes = static_cast<size_t>(segments) * 2 * sizeof(int32_t);
   auto round_up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  p->workspace_bytes =
-      round_up(o_bytes) + round_up(ml_bytes) + round_up(c0_bytes) + round_up(r0_bytes) + round_up(si_bytes);
+  p->workspace_bytes = round_up(o_bytes) + round_up(ml_bytes) + round_up(r0_bytes) + round_up(job_bytes);
   e = hipMalloc(&p->workspace, p->workspace_bytes);
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -221,11 +231,9 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   ws += round_up(o_bytes);
   p->part_ml = reinterpret_cast<float*>(ws);
   ws += round_up(ml_bytes);
-  p->seq_chunk0 = reinterpret_cast<int64_t*>(ws);
-  ws += round_up(c0_bytes);
   p->seq_row0 = reinterpret_cast<int32_t*>(ws);
   ws += round_up(r0_bytes);
-  p->seg_info = reinterpret_cast<int2*>(ws);
+  p->seg_merge = reinterpret_cast<int2*>(ws);
   *out_plan = p;
   return ATTN_OK;
 }
@@ -253,6 +261,7 @@ attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info) {
   info->merge_grid_size = plan->merge_grid;
   info->work_units = plan->max_units;
   info->packed = plan->variant.packed ? 1 : 0;
+  info->shared_kv = plan->variant.tile_waves > 0 ? 1 : 0;
   info->resident_groups_per_cu = plan->occupancy;
   info->compute_units = plan->num_cus;
   info->workspace_bytes = plan->workspace_bytes;
@@ -304,17 +313,16 @@ attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t*
   sp.max_q_len = d.max_q_len;
   sp.cols_per_block = plan->cols_per_block;
   sp.col_blocks = plan->col_blocks;
-  sp.wave_units = plan->variant.packed ? 1 : 0;
+  sp.unit_min_chunks = plan->unit_min_chunks;
   sp.max_units = plan->max_units;
-  sp.seq_chunk0 = plan->seq_chunk0;
   sp.seq_row0 = plan->seq_row0;
-  sp.seg_info = plan->seg_info;
+  sp.seg_merge = plan->seg_merge;
   sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
   sp.qk_scale_log2 = plan->sm_scale * 1.4426950408889634f;
 
   hipError_t e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream, plan->ev_start, plan->ev_stop);
   if (e == hipSuccess && plan->merge_grid > 0)
-    e = pa::launch_split_merge(plan->variant, sp, plan->merge_grid, plan->grid, stream);
+    e = pa::launch_split_merge(plan->variant, sp, plan->merge_grid, stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

@@ -196,39 +196,25 @@ __device__ SeqStart locate_seq(const StreamParams& p, int64_t pos, int lane, con
   return s;
 }
 
-// Workgroup 0 records where every sequence starts (and the total) for the
-// merge kernel, which runs after this kernel on the same stream.
+// Workgroup 0 records the first query row of every sequence for the merge
+// kernel, which runs after this kernel on the same stream.
 __device__ void write_seq_meta(const StreamParams& p, int lane) {
-  int64_t carry = 0;
   int rows = 0;
   for (int base = 0; base < p.num_seqs; base += 64) {
     const int b = base + lane;
-    int64_t nb = 0;
-    int qb = 0;
-    if (b < p.num_seqs) {
-      qb = p.q_lens[b];
-      nb = (int64_t)p.num_kv_heads * head_chunks(p, p.ctx_lens[b], qb);
-    }
-    const int64_t incl = wave_incl_scan64(nb, lane);
+    const int qb = (b < p.num_seqs) ? p.q_lens[b] : 0;
     const int qincl = (int)wave_incl_scan64(qb, lane);
-    if (b < p.num_seqs) {
-      p.seq_chunk0[b] = carry + incl - nb;
-      p.seq_row0[b] = rows + qincl - qb;
-    }
-    carry += __shfl(incl, 63);
+    if (b < p.num_seqs) p.seq_row0[b] = rows + qincl - qb;
     rows += __shfl(qincl, 63);
   }
-  if (lane == 0) p.seq_chunk0[p.num_seqs] = carry;
 }
 
-// Units that share the chunks: waves when each wave streams its own range
-// (packed decode; at least kMinChunksPerWave chunks each, so small problems
-// stay in one wave), workgroups otherwise.
-constexpr int kMinChunksPerWave = 8;
-
-__device__ __forceinline__ int work_units(const StreamParams& p, int64_t T, int grid) {
-  if (!p.wave_units) return grid;
-  const int64_t want = T / kMinChunksPerWave;
+// Units that share the chunks (waves when packed, workgroups otherwise):
+// one per unit_min_chunks chunks, at least one and at most max_units, so
+// small problems are not cut into pieces that cost more to merge than to
+// stream, and no unit's range is empty.
+__device__ __forceinline__ int work_units(const StreamParams& p, int64_t T) {
+  const int64_t want = T / p.unit_min_chunks;
   return (int)(want < 1 ? 1 : (want < p.max_units ? want : p.max_units));
 }
 
@@ -977,40 +963,425 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
   }
 }
 
+
+// ---- wide column blocks: each KV chunk shared by the waves through LDS ----
+// With more than 16 query columns per segment the NW waves of a workgroup
+// split the columns (NT 16-column tiles each, column 16 (wave NT + t) + ln)
+// and all of them walk every chunk of the piece.  The workgroup reads a
+// chunk from HBM once: its 2 (NKV + NVV) full-line 1 KB loads (the loads of
+// the register path) are spread over the waves, each thread converts its
+// bytes to bf16 once and stores them in LDS in MFMA operand order, one
+// 16-byte operand per lane and slab, so every operand read is a 16-byte LDS
+// read by consecutive lanes.  Raw chunks wait in a ring of R register
+// buffers; LDS holds two converted chunks, so the one barrier per chunk both
+// publishes chunk k and frees the buffer of chunk k - 1 for chunk k + 1.
+template <int D, int NW>
+struct TileGeo {
+  using GD = Geo<D>;
+  static constexpr int NL = 2 * (GD::NKV + GD::NVV);  // 1 KB loads per chunk
+  static constexpr int LPT = NL / NW;                   // loads per thread per chunk
+  static constexpr int KSL = 2 * GD::NSLAB;             // K operands: pages x slabs
+  static constexpr int SLOTS = KSL + GD::NVB;           // + V operands: 16-row blocks of d
+  static_assert(NL % NW == 0, "the loads of a chunk split evenly over the waves");
+};
+
+__device__ __forceinline__ bf16x4 fp8x4_to_bf16x4(uint32_t w) {
+  const bf16x2 a = fp8x2_to_bf16x2<false>(w);
+  const bf16x2 b = fp8x2_to_bf16x2<true>(w);
+  return bf16x4{a[0], a[1], b[0], b[1]};
+}
+
+// Workgroup barrier ordering LDS only: global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Like ring_loop, with the consumption of a buffer split from the work on
+// it: consume(k, slot) empties the buffer, the buffer is refilled, then
+// compute(k) runs while the refill is in flight.
+template <int NRING, class Issue, class Consume, class Compute>
+__device__ __forceinline__ void ring_loop_split(int nk, Issue&& issue, Consume&& consume, Compute&& compute) {
+  if (nk >= NRING) {
+#pragma unroll
+    for (int j = 0; j < NRING; ++j) issue(j, j);
+    int k = 0;
+    for (; k + 2 * NRING <= nk; k += NRING) {
+#pragma unroll
+      for (int j = 0; j < NRING; ++j) {
+        consume(k + j, j);
+        issue(k + j + NRING, j);
+        compute(k + j);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NRING; ++j) {
+      consume(k + j, j);
+      if (k + j + NRING < nk) issue(k + j + NRING, j);
+      compute(k + j);
+    }
+#pragma unroll
+    for (int j = 0; j < NRING; ++j)
+      if (k + NRING + j < nk) {
+        consume(k + NRING + j, j);
+        compute(k + NRING + j);
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NRING; ++j)
+      if (j < nk) issue(j, j);
+#pragma unroll
+    for (int j = 0; j < NRING; ++j)
+      if (j < nk) {
+        consume(j, j);
+        compute(j);
+      }
+  }
+}
+
+// Q^T as the B operand of one 16-column tile: lane (lq, ln) holds, per slab
+// s, the values d = lq D/4 + 8s .. +7 of its column's query row (the
+// contraction order of the K operand); fp32 Q is split into three bf16
+// parts whose sum is exact.
+template <int D, bool QF32>
+__device__ __forceinline__ void load_q_operand(const StreamParams& p, size_t qoff, bool valid,
+                                               bf16x8 (&op)[QF32 ? 3 : 1][Geo<D>::NSLAB]) {
+  using GD = Geo<D>;
+  if constexpr (QF32) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(p.q) + qoff);
+#pragma unroll
+    for (int s = 0; s < GD::NSLAB; ++s) {
+      float x[8];
+      if (valid) {
+        const u32x4 w0 = src[2 * s], w1 = src[2 * s + 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = __uint_as_float(w0[j]);
+          x[4 + j] = __uint_as_float(w1[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = 0.f;
+      }
+      split_q_f32(x, op[0][s], op[1][s], op[2][s]);
+    }
+  } else {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) + qoff);
+#pragma unroll
+    for (int s = 0; s < GD::NSLAB; ++s) {
+      const u32x4 w = valid ? src[s] : u32x4{0u, 0u, 0u, 0u};
+      op[0][s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+}
+
+template <int D, int NW, int NT, bool QF32, bool OUTF32, int R>
+__device__ __forceinline__ void run_piece_tile(const StreamParams& p, const PieceDesc& pc, int lane, int wave) {
+  using GD = Geo<D>;
+  using TG = TileGeo<D, NW>;
+  constexpr int NP = QF32 ? 3 : 1;
+  const int lq = lane >> 4;
+  const int ln = lane & 15;
+  const int h = pc.h;
+  const int L = pc.L;
+  const int Qb = pc.Q;
+  const int G = p.group;
+  const int ncols = G * Qb;
+  const int col0 = pc.cb * p.cols_per_block;
+  const int cols_here = min(p.cols_per_block, ncols - col0);
+  const int first_masked_key = L - Qb + col0 / G + 1;  // keys >= this are hidden from some column
+  const int npages = (L + kPageSize - 1) / kPageSize;
+
+  // ---- this wave's query columns ------------------------------------------
+  int lim[NT], qrow[NT], qhead[NT];
+  bool cvalid[NT];
+  bf16x8 qop[NT][NP][GD::NSLAB];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int rc = 16 * (wave * NT + t) + ln;
+    cvalid[t] = rc < cols_here;
+    const int gc = col0 + (cvalid[t] ? rc : 0);
+    const int i = gc / G;
+    const int g = gc - i * G;
+    lim[t] = cvalid[t] ? (L - Qb + i) : -1;
+    qrow[t] = pc.row0 + i;
+    qhead[t] = h * G + g;
+    load_q_operand<D, QF32>(p, ((size_t)qrow[t] * p.num_q_heads + qhead[t]) * D + (size_t)lq * GD::DQ, cvalid[t],
+                            qop[t]);
+  }
+
+  f32x4 o[NT][GD::NVB];
+  float m[NT], l[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m[t] = kNegInf;
+    l[t] = 0.f;
+#pragma unroll
+    for (int c = 0; c < GD::NVB; ++c) o[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- this thread's share of a chunk's loads -----------------------------
+  // load r is slot j = r NW + wave of the chunk: K of page j / NKV, 16-byte
+  // block j % NKV of the lane's quarter of d (slabs 2 (j % NKV) and +1), or V
+  // of page j' / NVV (j' = j - 2 NKV), the lane's values d = NVB ln + 4 i ..
+  // +3 (i = j' % NVV) for the 4 keys of its quarter.
+  uint32_t soff[TG::LPT];  // lane's byte offset inside the (page, head) chunk
+  int ldpg[TG::LPT];
+#pragma unroll
+  for (int r = 0; r < TG::LPT; ++r) {
+    const int j = r * NW + wave;
+    if (j < 2 * GD::NKV) {
+      ldpg[r] = j / GD::NKV;
+      soff[r] = k_in_chunk(ln, lq * GD::DQ + 16 * (j % GD::NKV), D);
+    } else {
+      const int jj = j - 2 * GD::NKV;
+      ldpg[r] = jj / GD::NVV;
+      soff[r] = v_in_chunk(4 * lq, GD::NVB * ln + 4 * (jj % GD::NVV), D);
+    }
+  }
+
+  __shared__ bf16x8 s_kv[2][TG::SLOTS][64];
+  // the previous piece may still read either buffer
+  lds_barrier();
+
+  const int32_t* bt = p.block_table + (size_t)pc.b * p.bt_stride;
+  const int c_begin = pc.c_begin;
+  const int nk = pc.c_end - c_begin;
+  // block-table batch: lane j holds the page of chunk k0 + j/2, position j%2,
+  // with that page's K and V scales
+  int32_t bt_v = 0;
+  float sk_v = 0.f, sv_v = 0.f;
+  auto load_batch = [&](int k0) {
+    const int k = k0 + (lane >> 1);
+    int32_t ph = 0;
+    float a = 0.f, bsc = 0.f;
+    if (k < nk) {
+      const int pg = min(2 * (c_begin + k) + (lane & 1), npages - 1);  // a missing second page repeats the first
+      ph = bt[pg];
+      const int64_t sidx = (int64_t)ph * p.num_kv_heads + h;
+      a = p.kv_scales[sidx];
+      bsc = p.kv_scales[p.v_scale_offset + sidx];
+    }
+    bt_v = ph;
+    sk_v = a;
+    sv_v = bsc;
+  };
+
+  u32x4 raw[R][TG::LPT];
+  float skr[R][2], svr[R][2];
+  auto issue = [&](int k, int j) {
+    if ((k & 31) == 0) load_batch(k);
+    const int e = 2 * (k & 31);
+#pragma unroll
+    for (int r = 0; r < TG::LPT; ++r) {
+      const int32_t ph = __builtin_amdgcn_readlane(bt_v, e + ldpg[r]);
+      const uint8_t* pool = (r * NW + wave < 2 * GD::NKV) ? p.k_pages : p.v_pages;
+      raw[j][r] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(pool + chunk_offset(ph, h, p.num_kv_heads, D) + soff[r]));
+    }
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      skr[j][pg] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sk_v), e + pg));
+      svr[j][pg] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sv_v), e + pg));
+    }
+  };
+
+  // scales of the chunk between its consume and compute (its ring buffer is
+  // refilled in between)
+  float csk[2], csv[2];
+  auto consume = [&](int k, int j) {
+    const int c = c_begin + k;
+    bf16x8 (*dst)[64] = s_kv[k & 1];
+#pragma unroll
+    for (int r = 0; r < TG::LPT; ++r) {
+      const u32x4 w = raw[j][r];
+      const int jj = r * NW + wave;
+      if (jj < 2 * GD::NKV) {
+        const int s0 = ldpg[r] * GD::NSLAB + 2 * (jj % GD::NKV);
+        dst[s0][lane] = fp8x8_to_bf16x8(w[0], w[1]);
+        dst[s0 + 1][lane] = fp8x8_to_bf16x8(w[2], w[3]);
+      } else {
+        // V bytes of keys >= L may be anything (NaN codes included): zero them
+        const int key0 = c * kChunk + 16 * ldpg[r] + 4 * lq;
+        uint32_t vm = 0xffffffffu;
+        if (c * kChunk + kChunk > L) {
+          vm = 0u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vm |= (key0 + e < L) ? (0xffu << (8 * e)) : 0u;
+        }
+        const int i = (jj - 2 * GD::NKV) % GD::NVV;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          reinterpret_cast<bf16x4*>(&dst[TG::KSL + 4 * i + e][lane])[ldpg[r]] = fp8x4_to_bf16x4(w[e] & vm);
+      }
+    }
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      csk[pg] = skr[j][pg];
+      csv[pg] = svr[j][pg];
+    }
+  };
+
+  auto compute = [&](int k) {
+    lds_barrier();
+    const bf16x8 (*kv)[64] = s_kv[k & 1];
+    const int c = c_begin + k;
+    // S^T = K Q^T for both pages
+    f32x4 sacc[2][NT];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sacc[pg][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < GD::NSLAB; ++s) {
+        const bf16x8 kb = kv[pg * GD::NSLAB + s][lane];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int part = 0; part < NP; ++part)
+            sacc[pg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[t][part][s], sacc[pg][t], 0, 0, 0);
+      }
+    }
+    // online softmax in log2 units with a lazy running max
+    const float fk0 = p.qk_scale_log2 * csk[0];
+    const float fk1 = p.qk_scale_log2 * csk[1];
+    const int key0 = c * kChunk + 4 * lq;  // key of register j: key0 + j (page 0), key0 + 16 + j (page 1)
+    const bool need_mask = (c * kChunk + kChunk - 1) >= first_masked_key;
+    bf16x8 pop_hi[NT], pop_lo[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = sacc[0][t][j] * fk0;
+        x[4 + j] = sacc[1][t][j] * fk1;
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = (key0 + j <= lim[t]) ? x[j] : kNegInf;
+          x[4 + j] = (key0 + 16 + j <= lim[t]) ? x[4 + j] : kNegInf;
+        }
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+      mx = max_over_lq(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyLog2)) {
+        const float mn = fmaxf(m[t], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[t] - ((mn == kNegInf) ? 0.f : mn));
+#pragma unroll
+        for (int cb2 = 0; cb2 < GD::NVB; ++cb2) o[t][cb2] *= alpha;
+        l[t] *= alpha;
+        m[t] = mn;
+      }
+      const float base = (m[t] == kNegInf) ? 0.f : m[t];
+      uint32_t phi[4], plo[4];
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const float pa0 = __builtin_amdgcn_exp2f(x[2 * k2] - base);
+        const float pa1 = __builtin_amdgcn_exp2f(x[2 * k2 + 1] - base);
+        l[t] += pa0 + pa1;
+        // P~ = p * V scale as bf16 hi + lo
+        const float sc = (k2 < 2) ? csv[0] : csv[1];
+        const float a = pa0 * sc;
+        const float bb = pa1 * sc;
+        phi[k2] = pack_bf16(a, bb);
+        plo[k2] = pack_bf16(a - bf16_lo(phi[k2]), bb - bf16_hi(phi[k2]));
+      }
+      pop_hi[t] = __builtin_bit_cast(bf16x8, u32x4{phi[0], phi[1], phi[2], phi[3]});
+      pop_lo[t] = __builtin_bit_cast(bf16x8, u32x4{plo[0], plo[1], plo[2], plo[3]});
+    }
+    // O^T += V^T P~^T
+#pragma unroll
+    for (int cblk = 0; cblk < GD::NVB; ++cblk) {
+      const bf16x8 va = kv[TG::KSL + cblk][lane];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        o[t][cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi[t], o[t][cblk], 0, 0, 0);
+        o[t][cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[t], o[t][cblk], 0, 0, 0);
+      }
+    }
+  };
+
+  ring_loop_split<R>(nk, issue, consume, compute);
+
+  // ---- write: final output, or this piece's partial -----------------------
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    l[t] = sum_over_lq(l[t]);
+    if (!cvalid[t]) continue;
+    const int rc = 16 * (wave * NT + t) + ln;
+    if (pc.whole) {
+      const float inv = 1.f / l[t];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const size_t off = ((size_t)qrow[t] * p.num_q_heads + qhead[t]) * D + (size_t)GD::NVB * (4 * lq + j);
+        if constexpr (OUTF32) {
+          float* dst = static_cast<float*>(p.out) + off;
+#pragma unroll
+          for (int c4 = 0; c4 < GD::NVB / 4; ++c4) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = o[t][4 * c4 + e][j] * inv;
+            *reinterpret_cast<f32x4*>(dst + 4 * c4) = v;
+          }
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(p.out) + off;
+          uint32_t w[GD::NVB / 2];
+#pragma unroll
+          for (int e = 0; e < GD::NVB / 2; ++e) w[e] = pack_bf16(o[t][2 * e][j] * inv, o[t][2 * e + 1][j] * inv);
+          if constexpr (GD::NVB == 8) {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+          } else {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+          }
+        }
+      }
+    } else {
+      float* po = p.part_o + ((size_t)pc.slot * p.cols_per_block + rc) * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float* dst = po + GD::NVB * (4 * lq + j);
+#pragma unroll
+        for (int c4 = 0; c4 < GD::NVB / 4; ++c4) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[t][4 * c4 + e][j];
+          *reinterpret_cast<f32x4*>(dst + 4 * c4) = v;
+        }
+      }
+      if (lq == 0) {
+        float* pm = p.part_ml + ((size_t)pc.slot * p.cols_per_block + rc) * 2;
+        pm[0] = m[t];
+        pm[1] = l[t];
+      }
+    }
+  }
+}
+
 }  // namespace
 
-// ---- attention kernel: one balanced chunk range per workgroup -------------
-// NCT = 0 is the packed decode layout (at most 4 query columns), otherwise
-// NCT 16-column tiles.  Packed and single-tile variants are held to 256
-// registers per wave (two waves per SIMD, eight per compute unit, each with
-// 24-32 KB of K+V in flight); wider tiles keep the whole register file for
-// their accumulators.
-template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32>
-__global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
-                             (NCT == 0 ? PACKED_WAVES_PER_SIMD : NCT == 1 ? 2 : 1)) void attn_stream_kernel(StreamParams p) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  if (blockIdx.x == 0 && wave == 0) write_seq_meta(p, lane);
-  const SeqLens c0 = load_seq(p, lane);
-  const int64_t T = total_chunks(p, lane, c0);
-  // this unit's share of the chunks: a wave's (packed) or the workgroup's
-  const int W = work_units(p, T, gridDim.x);
-  const int w = (NCT == 0) ? (int)blockIdx.x * kPackedWaves + wave : (int)blockIdx.x;
-  if (w >= W) return;
+// ---- the pieces of one unit's chunk range ---------------------------------
+// Unit w of W takes global chunks [floor(w T / W), floor((w+1) T / W)) and
+// runs run(piece) for the part of each segment inside that range, in order.
+// `leader` is the one lane of the unit that records, for each segment whose
+// first chunk lies in its range, where the segment's partials start and how
+// many units hold pieces of it (1: written whole).
+template <class Run>
+__device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, bool leader, int w, int W, int64_t T,
+                                            const SeqLens& c0, Run&& run) {
   const int64_t lo = (int64_t)w * T / W;
   const int64_t hi = (int64_t)(w + 1) * T / W;
   if (lo >= hi) return;
-
-  // walk the segments of [lo, hi)
   SeqStart ss = locate_seq(p, lo, lane, c0);
   int b = ss.b;
-  int64_t seq0 = ss.chunk0;
   int row0 = ss.row0;
   int L = ss.L;
   int Q = ss.Q;
-  int per_head = head_chunks(p, L, Q);
-  int64_t off = lo - seq0;
+  const int per_head = head_chunks(p, L, Q);
+  const int64_t off = lo - ss.chunk0;
   int h = (int)(off / per_head);
   int r = (int)(off - (int64_t)h * per_head);
   int cb = 0;
@@ -1035,20 +1406,12 @@ __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
     pc.whole = (r == 0) && (take == n);
     const int seg = (b * p.num_kv_heads + h) * p.col_blocks + cb;
     pc.slot = seg + w;
-    if (r == 0 && lane == 0 && (NCT == 0 || wave == 0)) {
-      // this unit holds the segment's first chunk: tell the merge kernel
-      // where the segment's partials start and how many units hold pieces
+    if (r == 0 && leader) {
+      // units w .. last hold the pieces; their partial slots are seg + w ..
       const int last = pc.whole ? w : wg_of_chunk(cur + n - 1, T, W);
-      p.seg_info[seg] = make_int2(seg + w, last - w + 1);
+      p.seg_merge[seg] = make_int2(seg + w, last - w + 1);
     }
-    if constexpr (NCT == 0) {
-      // at most 4 query columns: four pages per score tile
-      run_piece_packed<D, QF32, OUTF32, PACKED_RING>(p, pc, lane);
-    } else {
-      // ring depth: a single column tile leaves registers for three chunks
-      // in flight per wave, wider tiles for two
-      run_piece<D, (NCT == 0 ? 1 : NCT), DUPLO, QF32, OUTF32, (NCT == 1 ? 3 : 2)>(p, pc, lane, wave);
-    }
+    run(pc);
     cur += take;
     if (cur >= hi) break;
     // next non-empty segment
@@ -1069,96 +1432,185 @@ __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
   }
 }
 
+// ---- attention kernels -------------------------------------------------------
+// NCT = 0 is the packed decode layout (at most 4 query columns; each wave is
+// a unit), NCT = 1 one 16-column tile whose 4 waves take the chunks of a
+// piece in turn (the workgroup is the unit).  Both are held to 256 registers
+// per wave: two waves per SIMD, eight per compute unit.
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32>
+__global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
+                             (NCT == 0 ? PACKED_WAVES_PER_SIMD : 2)) void attn_stream_kernel(StreamParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = (NCT == 0) ? (int)blockIdx.x * kPackedWaves + wave : (int)blockIdx.x;
+  const bool leader = lane == 0 && (NCT == 0 || wave == 0);
+
+  if (blockIdx.x == 0 && wave == 0) write_seq_meta(p, lane);
+  const SeqLens c0 = load_seq(p, lane);
+  const int64_t T = total_chunks(p, lane, c0);
+  const int W = work_units(p, T);
+  if (w >= W) return;
+  walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
+    if constexpr (NCT == 0) {
+      // at most 4 query columns: four pages per score tile
+      run_piece_packed<D, QF32, OUTF32, PACKED_RING>(p, pc, lane);
+    } else {
+      run_piece<D, NCT, DUPLO, QF32, OUTF32, 3>(p, pc, lane, wave);
+    }
+  });
+}
+
+// Wide column blocks: NW waves share each chunk through LDS, NT tiles each,
+// two waves per SIMD.  Ring depth (raw chunks ahead of the one converted):
+// three with two waves per workgroup, six with four (a few workgroups per
+// compute unit must keep ~48 KB in flight each), two with two tiles per
+// wave, whose accumulators take the registers.
+#ifndef TILE_RING2
+#define TILE_RING2 3
+#endif
+#ifndef TILE_RING4
+#define TILE_RING4 6
+#endif
+#ifndef TILE_RING_WIDE
+#define TILE_RING_WIDE 2
+#endif
+template <int NW, int NT>
+struct TileCfg {
+  static constexpr int R = (NT == 2) ? TILE_RING_WIDE : (NW == 2 ? TILE_RING2 : TILE_RING4);
+  static constexpr int WAVES_PER_SIMD = 2;
+};
+
+template <int D, int NW, int NT, bool QF32, bool OUTF32>
+__global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void attn_tile_kernel(StreamParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = blockIdx.x;
+  const bool leader = lane == 0 && wave == 0;
+
+  if (w == 0 && wave == 0) write_seq_meta(p, lane);
+  const SeqLens c0 = load_seq(p, lane);
+  const int64_t T = total_chunks(p, lane, c0);
+  const int W = work_units(p, T);
+  if (w >= W) return;
+  walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
+    run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R>(p, pc, lane, wave);
+  });
+}
+
 // ---- log-sum-exp merge of the partials of one segment ---------------------
 // out = sum_k 2^(m_k - m) O_k / sum_k 2^(m_k - m) l_k,  m = max_k m_k, over
-// the pieces of a segment.  One workgroup per (segment, query column): its 8
-// groups of D/4 threads take the pieces k = g, g + 8, ... and merge them
-// online (4 d values per thread), then group 0 merges the 8 group results
-// through LDS in group order.  The result depends only on the pieces, not on
-// timing.  Segments that one attention workgroup finished alone are skipped.
-constexpr int kMergeGroups = 8;
+// the pieces k of a segment.  Workgroup (s, y) of 256 threads takes segment
+// s and its columns [y CW, (y+1) CW): CW = 1 for blocks of at most 4
+// columns (decode: few columns, many pieces), else the NG = 256 / (D/4)
+// columns its NG groups of D/4 threads cover.  With C columns here
+// (rounded up to a power of two), GPC = NG / C groups share a column, each
+// merging the pieces k = phase, phase + GPC, ... online (four loads in
+// flight), and the groups of a column are combined through LDS in phase
+// order.  The result depends only on the pieces, not on timing.  Segments
+// written whole by the attention kernel, and segments without chunks in
+// this forward (their entry is stale), are skipped.
+constexpr int kMergeThreads = 256;
 
 template <int D, bool OUTF32>
-__global__ __launch_bounds__(kMergeGroups * (D / 4)) void split_merge_kernel(StreamParams p, int attn_grid) {
+__global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(StreamParams p) {
   constexpr int V4 = D / 4;
-  const int rc = blockIdx.x % p.cols_per_block;
-  const int s = blockIdx.x / p.cols_per_block;
+  constexpr int NG = kMergeThreads / V4;
+  const int s = blockIdx.x;
   const int cb = s % p.col_blocks;
   const int h = (s / p.col_blocks) % p.num_kv_heads;
   const int b = s / (p.col_blocks * p.num_kv_heads);
-  // independent loads, issued together: lengths (a segment without chunks in
-  // this forward has no fresh metadata), the segment's metadata, the total
+  // independent loads, issued together
   const int L = p.ctx_lens[b];
   const int Q = p.q_lens[b];
-  const int2 si = p.seg_info[s];
-  const int64_t T = p.seq_chunk0[p.num_seqs];
+  const int2 sj = p.seg_merge[s];
   const int rows = p.seq_row0[b];
-  const int n = seg_chunks(L, Q, p.group, p.cols_per_block, cb);
   const int G = p.group;
   const int col0 = cb * p.cols_per_block;
-  if (n == 0 || col0 + rc >= G * Q) return;
-  const int nparts = si.y;
+  if (seg_chunks(L, Q, G, p.cols_per_block, cb) == 0) return;
+  const int slot0 = sj.x;
+  const int nparts = sj.y;
   if (nparts <= 1) return;  // written whole by the attention kernel
-  const int slot0 = si.x;
-  const int U = work_units(p, T, attn_grid);
-  const int w_first = slot0 - s;
-
+  const int cw = (gridDim.y == 1) ? p.cols_per_block : (p.cols_per_block <= 4 ? 1 : NG);
+  const int cy0 = blockIdx.y * cw;
+  const int cols_here = min(cw, min(p.cols_per_block, G * Q - col0) - cy0);
+  if (cols_here <= 0) return;
+  int cpass = 1;
+  while (cpass < cols_here) cpass <<= 1;
+  const int gpc = NG / cpass;
   const int grp = threadIdx.x / V4;
-  const int d4 = (threadIdx.x - grp * V4) * 4;
+  const int t4 = threadIdx.x - grp * V4;
+  const int d4 = t4 * 4;
+  const int cl = grp / gpc;
+  const int phase = grp - cl * gpc;
+  const int rc = cy0 + cl;  // column inside the block
+  const bool active = cl < cols_here;
+
   float mx = kNegInf;
   float lsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int k = grp; k < nparts; k += kMergeGroups) {
-    // with more units than chunks some ranges are empty: such a unit wrote
-    // no partial
-    if (T < U) {
-      const int64_t wk = w_first + k;
-      if ((wk * T) / U == ((wk + 1) * T) / U) continue;
+  if (active) {
+    for (int k0 = phase; k0 < nparts; k0 += 4 * gpc) {
+      float mkp[4], lkp[4];
+      f32x4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = k0 + q * gpc;
+        if (k < nparts) {
+          const size_t ri = (size_t)(slot0 + k) * p.cols_per_block + rc;
+          mkp[q] = p.part_ml[ri * 2];
+          lkp[q] = p.part_ml[ri * 2 + 1];
+          v[q] = *reinterpret_cast<const f32x4*>(p.part_o + ri * D + d4);
+        } else {
+          mkp[q] = kNegInf;
+          lkp[q] = 0.f;
+          v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float mn = fmaxf(mx, mkp[q]);
+        const float base = (mn == kNegInf) ? 0.f : mn;
+        const float fo = __builtin_amdgcn_exp2f(mx - base);
+        const float fk = __builtin_amdgcn_exp2f(mkp[q] - base);
+        lsum = lsum * fo + lkp[q] * fk;
+        acc = acc * fo + v[q] * fk;
+        mx = mn;
+      }
     }
-    const size_t ri = (size_t)(slot0 + k) * p.cols_per_block + rc;
-    const float mk = p.part_ml[ri * 2];
-    const float lk = p.part_ml[ri * 2 + 1];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_o + ri * D + d4);
-    const float mn = fmaxf(mx, mk);
-    const float base = (mn == kNegInf) ? 0.f : mn;
-    const float fo = __builtin_amdgcn_exp2f(mx - base);
-    const float fk = __builtin_amdgcn_exp2f(mk - base);
-    lsum = lsum * fo + lk * fk;
-    acc = acc * fo + v * fk;
-    mx = mn;
   }
-  __shared__ f32x4 s_acc[kMergeGroups][V4];
-  __shared__ float s_m[kMergeGroups], s_l[kMergeGroups];
-  s_acc[grp][threadIdx.x - grp * V4] = acc;
-  if (threadIdx.x == grp * V4) {
-    s_m[grp] = mx;
-    s_l[grp] = lsum;
+  if (gpc > 1) {
+    // combine the phases of each column in phase order
+    __shared__ f32x4 s_acc[NG][V4];
+    __shared__ float s_m[NG], s_l[NG];
+    s_acc[grp][t4] = acc;
+    if (t4 == 0) {
+      s_m[grp] = mx;
+      s_l[grp] = lsum;
+    }
+    __syncthreads();
+    if (phase != 0 || !active) return;
+    float m_all = kNegInf;
+    for (int j = 0; j < gpc; ++j) m_all = fmaxf(m_all, s_m[grp + j]);
+    const float base = (m_all == kNegInf) ? 0.f : m_all;
+    lsum = 0.f;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < gpc; ++j) {
+      const float f = __builtin_amdgcn_exp2f(s_m[grp + j] - base);
+      lsum += s_l[grp + j] * f;
+      acc += s_acc[grp + j][t4] * f;
+    }
   }
-  __syncthreads();
-  if (grp != 0) return;
-  float m_all = kNegInf;
-#pragma unroll
-  for (int j = 0; j < kMergeGroups; ++j) m_all = fmaxf(m_all, s_m[j]);
-  const float base = (m_all == kNegInf) ? 0.f : m_all;
-  float l_all = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < kMergeGroups; ++j) {
-    const float f = __builtin_amdgcn_exp2f(s_m[j] - base);
-    l_all += s_l[j] * f;
-    o += s_acc[j][threadIdx.x] * f;
-  }
-  const float inv = 1.f / l_all;
+  if (!active) return;
+  const float inv = 1.f / lsum;
   const int gc = col0 + rc;
   const int i = gc / G;
   const int gg = gc - i * G;
   const size_t off = ((size_t)(rows + i) * p.num_q_heads + h * G + gg) * D + d4;
   if constexpr (OUTF32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = o * inv;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = acc * inv;
   } else {
-    const uint32_t w0 = pack_bf16(o[0] * inv, o[1] * inv);
-    const uint32_t w1 = pack_bf16(o[2] * inv, o[3] * inv);
+    const uint32_t w0 = pack_bf16(acc[0] * inv, acc[1] * inv);
+    const uint32_t w1 = pack_bf16(acc[2] * inv, acc[3] * inv);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) = make_uint2(w0, w1);
   }
 }
@@ -1173,16 +1625,22 @@ static const void* kernel_d(const Variant& v) {
   return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false>);
 }
 
+template <int D, int NW, int NT>
+static const void* tile_d(const Variant& v) {
+  if (v.q_f32 && v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, true>);
+  if (v.q_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, false>);
+  if (v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, true>);
+  return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false>);
+}
+
 template <int D>
 static const void* kernel_tiles(const Variant& v) {
   if (v.packed) return kernel_d<D, 0, false>(v);
-  if (v.dup_lo) return kernel_d<D, 1, true>(v);
-  switch (v.col_tiles) {
-    case 1: return kernel_d<D, 1, false>(v);
-    case 2: return kernel_d<D, 2, false>(v);
-    case 4: return kernel_d<D, 4, false>(v);
-    default: return nullptr;
-  }
+  if (v.tile_waves == 2 && v.col_tiles == 1) return tile_d<D, 2, 1>(v);
+  if (v.tile_waves == 4 && v.col_tiles == 1) return tile_d<D, 4, 1>(v);
+  if (v.tile_waves == 4 && v.col_tiles == 2) return tile_d<D, 4, 2>(v);
+  if (v.tile_waves != 0 || v.col_tiles != 1) return nullptr;
+  return v.dup_lo ? kernel_d<D, 1, true>(v) : kernel_d<D, 1, false>(v);
 }
 
 static const void* stream_kernel(const Variant& v) {
@@ -1210,15 +1668,24 @@ hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int 
   return hipLaunchKernel(f, dim3(grid), dim3(64 * waves_per_group(v)), args, 0, stream);
 }
 
-hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, int attn_grid, hipStream_t stream) {
+// One workgroup per (segment, column) for blocks of at most 4 columns,
+// per (segment, 256 / (D/4) columns) otherwise.
+int merge_grid_y(const Variant& v, int cols_per_block) {
+  if (cols_per_block <= 4) return cols_per_block;
+  const int cw = kMergeThreads / (v.head_dim / 4);
+  return (cols_per_block + cw - 1) / cw;
+}
+
+hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  const dim3 block(kMergeGroups * (v.head_dim / 4));
+  const dim3 g(grid, merge_grid_y(v, p.cols_per_block));
+  const dim3 block(kMergeThreads);
   if (v.head_dim == 128) {
-    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<128, true>), dim3(grid), block, 0, stream, p, attn_grid);
-    else hipLaunchKernelGGL((split_merge_kernel<128, false>), dim3(grid), block, 0, stream, p, attn_grid);
+    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<128, true>), g, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_merge_kernel<128, false>), g, block, 0, stream, p);
   } else if (v.head_dim == 64) {
-    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<64, true>), dim3(grid), block, 0, stream, p, attn_grid);
-    else hipLaunchKernelGGL((split_merge_kernel<64, false>), dim3(grid), block, 0, stream, p, attn_grid);
+    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<64, true>), g, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_merge_kernel<64, false>), g, block, 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

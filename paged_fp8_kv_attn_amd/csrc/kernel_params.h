@@ -20,9 +20,8 @@ struct StreamParams {
   void* out;                   // [sum Q][Hq][D] bf16 or fp32
   float* part_o;               // [slots][cols_per_block][D] unnormalised partial outputs
   float* part_ml;              // [slots][cols_per_block][2] running max (log2 units), sum
-  int64_t* seq_chunk0;         // [B + 1] first global chunk of each sequence; [B] = total
   int32_t* seq_row0;           // [B] first query row of each sequence
-  int2* seg_info;              // [segments] written by the unit holding a segment's first
+  int2* seg_merge;             // [segments] written by the unit holding a segment's first
                                // chunk: (first partial slot, pieces; 1 = written whole)
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -32,7 +31,7 @@ struct StreamParams {
   int32_t max_q_len;
   int32_t cols_per_block;      // query columns (new token x head of a group) per workgroup
   int32_t col_blocks;          // column blocks of one (sequence, kv head)
-  int32_t wave_units;          // 1: each wave streams its own share (packed decode)
+  int32_t unit_min_chunks;     // units in use: total chunks / this, within [1, max_units]
   int32_t max_units;           // units sharing the chunks at most (waves or workgroups)
   int64_t v_scale_offset;      // P * Hkv: start of the V scales in kv_scales
   float qk_scale_log2;         // sm_scale * log2(e)
@@ -41,7 +40,8 @@ struct StreamParams {
 struct Variant {
   int head_dim;     // 64 or 128
   bool packed;      // at most 4 query columns: four pages share a score tile
-  int col_tiles;    // 1, 2 or 4 MFMA column tiles of 16
+  int tile_waves;   // > 0: waves sharing each KV chunk through LDS, col_tiles each
+  int col_tiles;    // 16-column MFMA tiles per wave (1, or 2 with tile_waves)
   bool dup_lo;      // low halves of P in spare columns (col_tiles == 1, <= 8 columns)
   bool q_f32;
   bool out_f32;
@@ -55,19 +55,21 @@ constexpr int kWavesPerGroup = 4;
 // chunk range, so the workgroup is only a unit of dispatch).
 constexpr int kPackedWaves = PACKED_GROUP_WAVES;
 
+inline int waves_per_group(const Variant& v) {
+  return v.packed ? kPackedWaves : v.tile_waves > 0 ? v.tile_waves : kWavesPerGroup;
+}
 
-// Attention kernel: `grid` workgroups share the key chunks of all segments
-// equally.  Partial slots needed: segments + grid.
-// With ev_start/ev_stop non-null they record the kernel's own start and end.
-inline int waves_per_group(const Variant& v) { return v.packed ? kPackedWaves : kWavesPerGroup; }
-
+// Attention kernel: the units of `grid` workgroups (waves when packed) share
+// the key chunks of all segments equally.  Partial slots needed: segments +
+// max_units.  With ev_start/ev_stop non-null they record the kernel's own
+// start and end.
 hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream,
                                    hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // Resident workgroups per compute unit for the variant's attention kernel.
 hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu);
-// Merge kernel: one workgroup per segment (`grid` = segments), for an
-// attention launch of `attn_grid` workgroups.
-hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, int attn_grid, hipStream_t stream);
+// Merge kernel: `grid` = segments workgroups along x, merge_grid_y along y.
+hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream);
+int merge_grid_y(const Variant& v, int cols_per_block);
 
 struct GatherParams {
   const uint8_t* k_pages;
