@@ -61,10 +61,16 @@ int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 constexpr int kChunkTokens = 32;  // keys per chunk (two pages)
 constexpr int kMinChunksPerGroup = 16;  // a workgroup's share is at least 4 chunks per wave
 constexpr int kMinChunksPerWave = 8;    // a wave's share in the packed layout
-// A shared-KV workgroup's share: wide column blocks write large partials
-// (columns x D fp32), so a unit streams at least 32 chunks (256 KB of K+V
-// at D = 128) per piece boundary it may cut.
-constexpr int kMinChunksPerTile = 32;
+// A shared-KV workgroup's share: at least 16 chunks (128 KB of K+V at
+// D = 128).  Wide column blocks write large partials (columns x D fp32) at
+// each piece boundary, but with fewer, longer units too few waves share a
+// compute unit to hide the latency of each chunk's load-convert-compute
+// chain (measured on MI355X: 16 beats 32 by 15-20% on MTP verification
+// and MQA decode, 8 gains nothing more).
+#ifndef TILE_MIN_CHUNKS
+#define TILE_MIN_CHUNKS 16
+#endif
+constexpr int kMinChunksPerTile = TILE_MIN_CHUNKS;
 
 attn_status_t validate_desc(const attn_plan_desc_t& d) {
   for (int r : d.reserved)

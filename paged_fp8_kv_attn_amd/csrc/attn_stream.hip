@@ -265,6 +265,17 @@ __device__ __forceinline__ void ring_loop(int nk, Issue&& issue, Step&& step) {
   }
 }
 
+// A block-table batch (page ids and page scales, one gather per 16-32
+// chunks) is waited for where it is loaded.  Its registers are read at
+// every refill; were the batch still pending there on some path, the
+// compiler, which cannot tell that path is rare, would make every refill
+// wait until only the newest chunk's loads are in flight, emptying the
+// ring.  Reading the registers in an empty asm completes the loads once
+// per batch instead.
+__device__ __forceinline__ void settle_batch(int32_t bt, float sk, float sv) {
+  __asm__ volatile("" : : "v"(bt), "v"(sk), "v"(sv));
+}
+
 // ---- one piece of a segment ----------------------------------------------
 
 struct PieceDesc {
@@ -386,6 +397,7 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
     bt_v = ph;
     sk_v = a;
     sv_v = bsc;
+    settle_batch(bt_v, sk_v, sv_v);
   };
   u32x4 kbuf[NBUF][2][GD::NKV], vbuf[NBUF][2][GD::NVV];
   float skb[NBUF][2], svb[NBUF][2];
@@ -779,6 +791,7 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
     bt_v = ph;
     sk_v = a;
     sv_v = bsc;
+    settle_batch(bt_v, sk_v, sv_v);
   };
 
   u32x4 kbuf[NRING][4][GD::NKV], vbuf[NRING][4][GD::NVV];
@@ -1166,6 +1179,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
     bt_v = ph;
     sk_v = a;
     sv_v = bsc;
+    settle_batch(bt_v, sk_v, sv_v);
   };
 
   u32x4 raw[R][TG::LPT];
