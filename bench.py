@@ -90,16 +90,22 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counter_summary_path(workload: str) -> str:
-    return os.path.join(PROFILES, f"attn_stream_kernel_{workload}_hbm_counters.txt")
+def attention_kernel_name(info: dict) -> str:
+    """The attention kernel the plan launches: the shared-KV tile kernel for
+    blocks of more than 16 query columns, the streaming kernel otherwise."""
+    return "attn_tile_kernel" if info.get("shared_kv") else "attn_stream_kernel"
 
 
-def committed_traffic(workload: str):
+def counter_summary_path(workload: str, kernel: str = "attn_stream_kernel") -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload}_hbm_counters.txt")
+
+
+def committed_traffic(workload: str, kernel: str = "attn_stream_kernel"):
     """HBM bytes per launch of the attention kernel from the committed
     rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE per dispatch, each
     scaled by what the same counter reads for a plain device copy of known
     size), if it was taken on the current kernel source; otherwise None."""
-    path = counter_summary_path(workload)
+    path = counter_summary_path(workload, kernel)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -379,14 +385,15 @@ def main():
     k_gbs = counts["bytes"] / (attn_ms * 1e-3) / 1e9
     k_tflops = counts["flops"] / (attn_ms * 1e-3) / 1e12
     prefill_like = counts["flops"] / max(1, counts["bytes"]) > 312  # above the bf16 ridge point
-    traffic = committed_traffic(w.name)
+    kernel_name = attention_kernel_name(plan.info())
+    traffic = committed_traffic(w.name, kernel_name)
     if prefill_like:
         roof = {"bound": "mfma", "achieved": k_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": k_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": k_gbs / HBM_PEAK_GBS, "traffic": traffic}
-    roof.update({"kernel": "attn_stream_kernel", "kernel_avg_us": attn_ms * 1e3,
+    roof.update({"kernel": kernel_name, "kernel_avg_us": attn_ms * 1e3,
                  "kernel_median_us": float(np.median(kernel_ms)) * 1e3,
                  "kernel_min_us": float(np.min(kernel_ms)) * 1e3, "kernel_max_us": float(np.max(kernel_ms)) * 1e3,
                  "algorithmic_bytes_per_launch": counts["bytes"],
