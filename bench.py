@@ -12,6 +12,9 @@ resident in HBM before timing starts; each forward reads a different copy of
 the KV pool from a rotation set of >= 1 GiB so that neither L2 nor the
 256 MB Infinity Cache can serve the KV.  Forwards are launched as one HIP
 graph of K nodes (``--eager`` launches them one by one from Python).
+``--workload prefill_mqa_mix`` makes a step of two forwards enqueued back to
+back on one stream: the 8 x 512-token prefill chunk, then the 64-sequence
+MQA decode batch (two plans, since their head counts differ).
 
 Prints one JSON line (rank 0): metric/value (algorithmic HBM GB/s of the
 whole step), query tokens/s, the roofline of the attention kernel (its own
@@ -43,6 +46,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATION_BYTES = 1 << 30
 KERNEL_SOURCE = os.path.join(ROOT, "paged_fp8_kv_attn_amd", "csrc", "attn_stream.hip")
 PROFILES = os.path.join(ROOT, "profiles")
+# workloads made of several forwards per step, enqueued back to back on one
+# stream: the chunked-prefill chunk and the MQA decode batch of one serving
+# step (two plans: their head counts differ)
+COMPOSITE = {"prefill_mqa_mix": ["prefill_chunk", "mqa_decode"]}
 
 
 def algorithmic_counts(w) -> dict:
@@ -290,31 +297,44 @@ def main():
     from synth import make_workload
 
     load_library()
-    t_gen = time.perf_counter()
-    w = make_workload(args.workload, keep_logical=False)
-    t_gen = time.perf_counter() - t_gen
-    counts = algorithmic_counts(w)
-
-    plan = Plan(num_seqs=w.num_seqs, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-                num_pages=w.num_pages, max_pages_per_seq=w.max_pages_per_seq, max_q_len=w.max_q_len,
-                max_ctx_len=w.max_ctx_len, q_dtype=w.q_dtype, out_dtype=w.out_dtype, sm_scale=w.sm_scale,
-                num_kv_splits=w.num_kv_splits)
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    q = w.q.to(dev)
-    bt = t(w.block_table)
-    ctx = t(w.ctx_lens)
-    ql = t(w.q_lens)
-    k0, v0, s0 = t(w.k_pages), t(w.v_pages), t(w.kv_scales)
-    pool_bytes = k0.numel() + v0.numel() + s0.numel() * 4
-    copies = max(2, math.ceil(ROTATION_BYTES / pool_bytes))
-    pools = [(k0, v0, s0)] + [(k0.clone(), v0.clone(), s0.clone()) for _ in range(copies - 1)]
-    out_dt = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
-    out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=out_dt, device=dev)
+    names = COMPOSITE.get(args.workload, [args.workload])
     stream = torch.cuda.current_stream()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
 
-    def fwd(i):
-        k, v, s = pools[i % copies]
-        plan.forward(q, k, v, s, bt, ctx, ql, out, stream=stream)
+    class Part:
+        """One forward of the step: a workload, its plan, its inputs in HBM
+        and a rotation of KV pool copies of >= 1 GiB."""
+
+        def __init__(self, name):
+            w = make_workload(name, keep_logical=False)
+            self.w = w
+            self.counts = algorithmic_counts(w)
+            self.plan = Plan(num_seqs=w.num_seqs, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                             head_dim=w.head_dim, num_pages=w.num_pages, max_pages_per_seq=w.max_pages_per_seq,
+                             max_q_len=w.max_q_len, max_ctx_len=w.max_ctx_len, q_dtype=w.q_dtype,
+                             out_dtype=w.out_dtype, sm_scale=w.sm_scale, num_kv_splits=w.num_kv_splits)
+            self.q = w.q.to(dev)
+            self.bt = t(w.block_table)
+            self.ctx = t(w.ctx_lens)
+            self.ql = t(w.q_lens)
+            k0, v0, s0 = t(w.k_pages), t(w.v_pages), t(w.kv_scales)
+            pool_bytes = k0.numel() + v0.numel() + s0.numel() * 4
+            self.copies = max(2, math.ceil(ROTATION_BYTES / pool_bytes))
+            self.pools = [(k0, v0, s0)] + [(k0.clone(), v0.clone(), s0.clone()) for _ in range(self.copies - 1)]
+            out_dt = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
+            self.out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=out_dt, device=dev)
+            self.kernel = attention_kernel_name(self.plan.info())
+
+        def forward(self, i, st):
+            k, v, s_ = self.pools[i % self.copies]
+            self.plan.forward(self.q, k, v, s_, self.bt, self.ctx, self.ql, self.out, stream=st)
+
+    parts = [Part(n) for n in names]
+    counts = {key: sum(pt.counts[key] for pt in parts) for key in parts[0].counts}
+
+    def fwd(i, st=stream):
+        for pt in parts:
+            pt.forward(i, st)
 
     for i in range(args.warmup):
         fwd(i)
@@ -329,8 +349,7 @@ def main():
 
         def body():
             for i in range(args.steps):
-                k, v, s = pools[i % copies]
-                plan.forward(q, k, v, s, bt, ctx, ql, out, stream=cap)
+                fwd(i, cap)
 
         graph.capture(cap, body)
         graph.launch(stream)  # one untimed launch of the captured steps
@@ -351,14 +370,13 @@ def main():
     total_ms = e0.elapsed_time(e1)
     ms = total_ms / args.steps
 
-    # Timed region 2: the same K steps launched one by one, each with a pair
-    # of HIP events that the library attaches to its attention kernel's own
-    # dispatch (they take that kernel's start and end timestamps).  A sleep
-    # kernel queued in front lets the host enqueue every step before the GPU
-    # reaches them, so the steps run back to back as in region 1.
+    # Timed region 2: the same K steps launched one by one, each attention
+    # kernel with a pair of HIP events that the library attaches to that
+    # kernel's own dispatch (they take its start and end timestamps).  A
+    # sleep kernel queued in front lets the host enqueue every step before
+    # the GPU reaches them, so the steps run back to back as in region 1.
     hipt = HipGraph()
-    k_start = [hipt.event() for _ in range(args.steps)]
-    k_stop = [hipt.event() for _ in range(args.steps)]
+    ev = [([hipt.event() for _ in range(args.steps)], [hipt.event() for _ in range(args.steps)]) for _ in parts]
     torch.cuda.synchronize()
     cal0 = torch.cuda.Event(enable_timing=True)
     cal1 = torch.cuda.Event(enable_timing=True)
@@ -367,38 +385,53 @@ def main():
     cal1.record(stream)
     torch.cuda.synchronize()
     sleep_ms_per_unit = cal0.elapsed_time(cal1) / (1 << 20)
-    head_start_ms = 5.0 + 0.05 * args.steps  # generous: ~50 us of host time per step
+    head_start_ms = 5.0 + 0.05 * args.steps * len(parts)  # generous: ~50 us of host time per forward
     torch.cuda._sleep(int(head_start_ms / max(sleep_ms_per_unit, 1e-9)))
     for i in range(args.steps):
-        plan.set_kernel_events(k_start[i], k_stop[i])
-        fwd(i)
-    plan.set_kernel_events(None, None)
+        for pt, (starts, stops) in zip(parts, ev):
+            pt.plan.set_kernel_events(starts[i], stops[i])
+            pt.forward(i, stream)
+    for pt in parts:
+        pt.plan.set_kernel_events(None, None)
     torch.cuda.synchronize()
-    kernel_ms = [hipt.elapsed_ms(a, b) for a, b in zip(k_start, k_stop)]
-    for e in k_start + k_stop:
-        hipt.destroy_event(e)
-    attn_ms = float(np.mean(kernel_ms))
+    for pt, (starts, stops) in zip(parts, ev):
+        pt.kernel_ms = [hipt.elapsed_ms(a, b) for a, b in zip(starts, stops)]
+        pt.attn_ms = float(np.mean(pt.kernel_ms))
+        for e in starts + stops:
+            hipt.destroy_event(e)
+
+    def roofline(pt, traffic):
+        c = pt.counts
+        k_gbs = c["bytes"] / (pt.attn_ms * 1e-3) / 1e9
+        k_tflops = c["flops"] / (pt.attn_ms * 1e-3) / 1e12
+        if c["flops"] / max(1, c["bytes"]) > 312:  # above the bf16 ridge point
+            roof = {"bound": "mfma", "achieved": k_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": k_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
+        else:
+            roof = {"bound": "hbm", "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": k_gbs / HBM_PEAK_GBS, "traffic": traffic}
+        roof.update({"kernel": pt.kernel, "kernel_avg_us": pt.attn_ms * 1e3,
+                     "kernel_median_us": float(np.median(pt.kernel_ms)) * 1e3,
+                     "kernel_min_us": float(np.min(pt.kernel_ms)) * 1e3,
+                     "kernel_max_us": float(np.max(pt.kernel_ms)) * 1e3,
+                     "algorithmic_bytes_per_launch": c["bytes"],
+                     "algorithmic_flops_per_launch": c["flops"], "launches_per_step": 1})
+        return roof
+
+    # the dominant kernel: the attention kernel with the largest share of the step
+    dom = max(parts, key=lambda pt: pt.attn_ms)
+    roof = roofline(dom, committed_traffic(dom.w.name, dom.kernel))
+    if len(parts) > 1:
+        roof["workload_part"] = dom.w.name
 
     gbs = counts["bytes"] / (ms * 1e-3) / 1e9
     tflops = counts["flops"] / (ms * 1e-3) / 1e12
     qtok = counts["query_tokens"] / (ms * 1e-3)
-    k_gbs = counts["bytes"] / (attn_ms * 1e-3) / 1e9
-    k_tflops = counts["flops"] / (attn_ms * 1e-3) / 1e12
-    prefill_like = counts["flops"] / max(1, counts["bytes"]) > 312  # above the bf16 ridge point
-    kernel_name = attention_kernel_name(plan.info())
-    traffic = committed_traffic(w.name, kernel_name)
-    if prefill_like:
-        roof = {"bound": "mfma", "achieved": k_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": k_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
+    if len(parts) == 1:
+        config = workload_config(parts[0].w)
     else:
-        roof = {"bound": "hbm", "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": k_gbs / HBM_PEAK_GBS, "traffic": traffic}
-    roof.update({"kernel": kernel_name, "kernel_avg_us": attn_ms * 1e3,
-                 "kernel_median_us": float(np.median(kernel_ms)) * 1e3,
-                 "kernel_min_us": float(np.min(kernel_ms)) * 1e3, "kernel_max_us": float(np.max(kernel_ms)) * 1e3,
-                 "algorithmic_bytes_per_launch": counts["bytes"],
-                 "algorithmic_flops_per_launch": counts["flops"], "launches_per_step": 1})
-
+        config = {"workload": args.workload, "parts": [workload_config(pt.w) for pt in parts],
+                  "order": "back to back on one stream, in the order listed"}
     res = {
         "metric": METRIC,
         "value": gbs,
@@ -412,19 +445,25 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": workload_config(w),
+        "config": config,
         "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
         "query_tokens_per_s": qtok,
         "tflops": tflops,
         "launch": "graph" if graph is not None else "eager",
-        "kv_pool_copies": copies,
-        "plan": plan.info(),
+        "kv_pool_copies": [pt.copies for pt in parts] if len(parts) > 1 else parts[0].copies,
+        "plan": [pt.plan.info() for pt in parts] if len(parts) > 1 else parts[0].plan.info(),
         "kernel_source_sha256_16": source_hash(),
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if len(parts) > 1:
+        res["parts"] = [{"workload": pt.w.name, "roofline": roofline(pt, committed_traffic(pt.w.name, pt.kernel))}
+                        for pt in parts]
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, counts, args.cpu_seconds)
+        # the oracle on the first part (the dominant one for the mixed workload)
+        res["cpu_baseline"] = cpu_baseline(dom.w, dom.counts, args.cpu_seconds)
+        if len(parts) > 1:
+            res["cpu_baseline"]["sample"] += f" (workload part {dom.w.name})"
     line = json.dumps(res)
     print(line, flush=True)
     if args.json_out:
@@ -433,7 +472,8 @@ def main():
     hipt.close()
     if graph is not None:
         graph.close()
-    plan.close()
+    for pt in parts:
+        pt.plan.close()
 
 
 if __name__ == "__main__":
