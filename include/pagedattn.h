@@ -128,8 +128,9 @@ typedef struct {
                                      1024 / head_dim columns */
   int32_t work_units;             /* units sharing the chunks at most: waves when packed,
                                      workgroups otherwise */
-  int32_t packed;                 /* 1: at most 4 query columns, four pages per score tile,
-                                     one wave per chunk range */
+  int32_t packed;                 /* > 0: at most 4 query columns, four pages per score
+                                     tile, one wave per chunk range, this many groups
+                                     of four pages in flight per wave (1 or 2) */
   int32_t shared_kv;              /* 1: more than 16 query columns; the waves of a
                                      workgroup split the columns and share each KV
                                      chunk through LDS */

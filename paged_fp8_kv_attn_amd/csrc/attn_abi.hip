@@ -129,6 +129,7 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   if (cols <= 4) {  // four pages per score tile
     v.col_tiles = 1;
     v.packed = true;
+    v.packed_ring = 2;  // one wave per SIMD, two groups in flight; see below
     p->cols_per_block = static_cast<int>(cols);
   } else if (cols <= 8) {  // hi parts of P in columns 0..7, lo parts in 8..15
     v.col_tiles = 1;
@@ -183,6 +184,18 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   // the largest lengths, so that small problems are not split at all.
   hipError_t e = hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e == hipSuccess) e = pa::stream_attention_occupancy(v, &p->occupancy);
+  if (e == hipSuccess && v.packed && d.num_kv_splits > 0) {
+    // Packed decode with two groups in flight holds one wave per SIMD; when a
+    // forced split count asks for more units than that resident at once,
+    // one group per wave at two waves per SIMD runs them in a single round.
+    const int64_t resident = static_cast<int64_t>(p->num_cus) * std::max(p->occupancy, 1) * pa::kPackedWaves;
+    const int64_t forced = static_cast<int64_t>(d.num_seqs) * d.num_kv_heads * d.num_kv_splits;
+    if (forced > resident) {
+      v.packed_ring = 1;
+      p->variant = v;
+      e = pa::stream_attention_occupancy(v, &p->occupancy);
+    }
+  }
   if (e != hipSuccess) {
     delete p;
     return hip_fail(e);
@@ -266,7 +279,7 @@ attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info) {
   info->grid_size = plan->grid;
   info->merge_grid_size = plan->merge_grid;
   info->work_units = plan->max_units;
-  info->packed = plan->variant.packed ? 1 : 0;
+  info->packed = plan->variant.packed ? plan->variant.packed_ring : 0;
   info->shared_kv = plan->variant.tile_waves > 0 ? 1 : 0;
   info->resident_groups_per_cu = plan->occupancy;
   info->compute_units = plan->num_cus;

@@ -674,16 +674,11 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
 // piece in groups of two chunks (four pages, 64 keys); keys at or past the
 // piece's end (or L) are masked.
 constexpr float kLazyLog2 = 8.f;
-// Packed decode tuning, measured on MI355X: one group of four pages (16 KB
-// of K+V) in flight per wave and two waves per SIMD.  Deeper rings (or one
-// wave per SIMD with a deeper ring) overfill the memory queues: latency grows,
-// bandwidth does not, and the slowest waves finish later.
-#ifndef PACKED_RING
-#define PACKED_RING 1
-#endif
-#ifndef PACKED_WAVES_PER_SIMD
-#define PACKED_WAVES_PER_SIMD 2
-#endif
+// Packed decode tuning, measured on MI355X: either one group of four pages
+// (16 KB of K+V) in flight per wave at two waves per SIMD, or two groups at
+// one wave per SIMD (the plan takes the second when its units fit on the
+// GPU at once: ~3% faster on batch-32 decode).  Deeper rings overfill the
+// memory queues: latency grows, bandwidth does not.
 
 __device__ __forceinline__ float dpp_ror4(float x) {
   return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x124 /*row_ror:4*/, 0xf, 0xf, false));
@@ -1448,12 +1443,13 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
 
 // ---- attention kernels -------------------------------------------------------
 // NCT = 0 is the packed decode layout (at most 4 query columns; each wave is
-// a unit), NCT = 1 one 16-column tile whose 4 waves take the chunks of a
-// piece in turn (the workgroup is the unit).  Both are held to 256 registers
-// per wave: two waves per SIMD, eight per compute unit.
-template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32>
+// a unit) with PR groups in flight per wave, NCT = 1 one 16-column tile whose
+// 4 waves take the chunks of a piece in turn (the workgroup is the unit).
+// Two waves per SIMD (256 registers each), one for the packed layout with
+// two groups in flight.
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int PR>
 __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
-                             (NCT == 0 ? PACKED_WAVES_PER_SIMD : 2)) void attn_stream_kernel(StreamParams p) {
+                             (NCT == 0 ? (PR == 1 ? 2 : 1) : 2)) void attn_stream_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int w = (NCT == 0) ? (int)blockIdx.x * kPackedWaves + wave : (int)blockIdx.x;
@@ -1467,9 +1463,9 @@ __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
   walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
     if constexpr (NCT == 0) {
       // at most 4 query columns: four pages per score tile
-      run_piece_packed<D, QF32, OUTF32, PACKED_RING>(p, pc, lane);
+      run_piece_packed<D, QF32, OUTF32, PR>(p, pc, lane);
     } else {
-      run_piece<D, NCT, DUPLO, QF32, OUTF32, 3>(p, pc, lane, wave);
+      run_piece<D, NCT, DUPLO, QF32, OUTF32, 2>(p, pc, lane, wave);
     }
   });
 }
@@ -1631,12 +1627,12 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(StreamParams
 
 // ---- dispatch --------------------------------------------------------------
 
-template <int D, int NCT, bool DUPLO>
+template <int D, int NCT, bool DUPLO, int PR = 1>
 static const void* kernel_d(const Variant& v) {
-  if (v.q_f32 && v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, true>);
-  if (v.q_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, false>);
-  if (v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, true>);
-  return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false>);
+  if (v.q_f32 && v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, true, PR>);
+  if (v.q_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, false, PR>);
+  if (v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, true, PR>);
+  return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR>);
 }
 
 template <int D, int NW, int NT>
@@ -1649,7 +1645,7 @@ static const void* tile_d(const Variant& v) {
 
 template <int D>
 static const void* kernel_tiles(const Variant& v) {
-  if (v.packed) return kernel_d<D, 0, false>(v);
+  if (v.packed) return v.packed_ring == 2 ? kernel_d<D, 0, false, 2>(v) : kernel_d<D, 0, false, 1>(v);
   if (v.tile_waves == 2 && v.col_tiles == 1) return tile_d<D, 2, 1>(v);
   if (v.tile_waves == 4 && v.col_tiles == 1) return tile_d<D, 4, 1>(v);
   if (v.tile_waves == 4 && v.col_tiles == 2) return tile_d<D, 4, 2>(v);

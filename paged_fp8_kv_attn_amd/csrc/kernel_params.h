@@ -40,6 +40,7 @@ struct StreamParams {
 struct Variant {
   int head_dim;     // 64 or 128
   bool packed;      // at most 4 query columns: four pages share a score tile
+  int packed_ring;  // packed: groups of four pages in flight per wave (1 or 2)
   int tile_waves;   // > 0: waves sharing each KV chunk through LDS, col_tiles each
   int col_tiles;    // 16-column MFMA tiles per wave (1, or 2 with tile_waves)
   bool dup_lo;      // low halves of P in spare columns (col_tiles == 1, <= 8 columns)
