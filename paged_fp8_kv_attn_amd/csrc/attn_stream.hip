@@ -1,7 +1,7 @@
 // Paged FP8-KV attention for gfx950: the keys of every (sequence, kv head,
 // block of query columns) are cut into 32-key chunks, the chunks of all of
-// them are laid end to end, and each workgroup streams an equal contiguous
-// range of that list, KV going from HBM straight into MFMA operand registers.
+// them are laid end to end, and each work unit streams an equal contiguous
+// range of that list.
 //
 // Follows the attention section of the Atlas engine article (ainews.cool,
 // "技术深度解析": a FlashAttention-2 variant with dedicated MQA/GQA kernels and
@@ -11,17 +11,23 @@
 //
 // Shape of the work.  The G = Hq/Hkv query heads of a kv head, times the Q_b
 // new tokens of a sequence, form G*Q_b "query columns" that all read the same
-// keys.  A segment is one (sequence, kv head, block of up to 16*col_tiles
-// columns) with its keys; it owns n = ceil(kv_end / 32) chunks.  Segments are
-// ordered (sequence, kv head, column block) and workgroup w of W takes global
-// chunks [floor(w T / W), floor((w+1) T / W)) of the T in total, so every
-// workgroup does the same amount of streaming whatever the length mix.  A
-// workgroup walks the pieces of segments in its range; its 4 waves take the
-// chunks of a piece in turn and merge through LDS at the piece's end.  A
-// segment that lies inside one workgroup's range is written to `out`
-// directly; otherwise each workgroup writes an unnormalised partial into slot
-// (segment + w), unique because ranges and segments are both ordered, and
-// the merge kernel combines them by log-sum-exp.
+// keys.  A segment is one (sequence, kv head, block of columns) with its
+// keys; it owns n = ceil(kv_end / 32) chunks.  Segments are ordered
+// (sequence, kv head, column block) and unit w of W takes global chunks
+// [floor(w T / W), floor((w+1) T / W)) of the T in total, so every unit does
+// the same amount of streaming whatever the length mix.  A segment that lies
+// inside one unit's range is written to `out` directly; otherwise each unit
+// writes an unnormalised partial into slot (segment + w), unique because
+// ranges and segments are both ordered, and the merge kernel combines them by
+// log-sum-exp.  Three kernel families share this schedule:
+//   * packed decode (at most 4 columns): each wave is a unit; four pages share
+//     one 16x16 score tile (run_piece_packed);
+//   * one 16-column tile (5..16 columns): the workgroup is the unit, its
+//     waves take the chunks of a piece in turn and merge through LDS
+//     (run_piece);
+//   * shared KV (more than 16 columns): the workgroup is the unit, its waves
+//     split the columns and share each chunk, converted to bf16 once, through
+//     LDS (run_piece_tile).
 //
 // Per chunk, in each wave (lane = 16*lq + ln):
 //   * K: lane reads the bytes of token slot ln at d in [lq*D/4, (lq+1)*D/4)
