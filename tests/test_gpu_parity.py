@@ -83,6 +83,10 @@ EDGE = [
     ([1, 4], [129, 64], 4, 1, 64, "f32", "bf16"),
     ([3, 1], [200, 333], 12, 4, 128, "bf16", "f32"),
     ([33, 20], [33, 100], 4, 2, 128, "bf16", "bf16"),  # prefill from empty cache
+    # shared-KV tile kernels with fp32 Q and/or output
+    ([5, 2], [400, 70], 40, 8, 128, "f32", "f32"),  # 25 columns
+    ([1, 1, 1], [700, 64, 2100], 64, 1, 128, "f32", "bf16"),  # 64 columns, split segments
+    ([40, 7], [300, 800], 4, 2, 64, "bf16", "f32"),  # 80 columns, D = 64
 ]
 
 
