@@ -123,9 +123,10 @@ typedef struct {
   int32_t num_segments;           /* B * Hkv * col_blocks */
   int32_t grid_size;              /* workgroups of the attention kernel */
   int32_t merge_grid_size;        /* merge kernel workgroups along x, one per segment
-                                     (0: not launched); along y one per column for
-                                     blocks of at most 4 columns, else one per
-                                     1024 / head_dim columns */
+                                     (0: not launched); along y one per slice of the
+                                     block's columns: single columns for blocks of at
+                                     most 4 columns or with many pieces per segment,
+                                     else up to 1024 / head_dim columns */
   int32_t work_units;             /* units sharing the chunks at most: waves when packed,
                                      workgroups otherwise */
   int32_t packed;                 /* > 0: at most 4 query columns, four pages per score

@@ -41,6 +41,7 @@ struct attn_plan_s {
   int32_t* seq_row0;
   int2* seg_merge;
   int merge_grid;
+  int merge_cols;  // query columns per merge workgroup
   hipEvent_t ev_start;  // optional: recorded around the attention kernel
   hipEvent_t ev_stop;
 };
@@ -226,8 +227,10 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   }
   p->max_units = static_cast<int>(units);
   p->grid = static_cast<int>(ceil_div(units * unit_waves, wpg));
-  // merge: one workgroup per segment (and slice of its columns)
+  // merge: one workgroup per segment (and slice of its columns); segments
+  // with many pieces on average get fewer columns per workgroup
   p->merge_grid = units > 1 ? p->num_segments : 0;
+  p->merge_cols = pa::merge_cols_for(v, p->cols_per_block, (units + segments - 1) / segments);
 
   // Workspace, allocated once: partial slots (segments + units of them, one
   // per (segment, unit) pair that can occur), each sequence's first query
@@ -332,6 +335,7 @@ attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t*
   sp.max_q_len = d.max_q_len;
   sp.cols_per_block = plan->cols_per_block;
   sp.col_blocks = plan->col_blocks;
+  sp.merge_cols = plan->merge_cols;
   sp.unit_min_chunks = plan->unit_min_chunks;
   sp.max_units = plan->max_units;
   sp.seq_row0 = plan->seq_row0;

@@ -1516,10 +1516,10 @@ __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void at
 // ---- log-sum-exp merge of the partials of one segment ---------------------
 // out = sum_k 2^(m_k - m) O_k / sum_k 2^(m_k - m) l_k,  m = max_k m_k, over
 // the pieces k of a segment.  Workgroup (s, y) of 256 threads takes segment
-// s and its columns [y CW, (y+1) CW): CW = 1 for blocks of at most 4
-// columns (decode: few columns, many pieces), else the NG = 256 / (D/4)
-// columns its NG groups of D/4 threads cover.  With C columns here
-// (rounded up to a power of two), GPC = NG / C groups share a column, each
+// s and its columns [y CW, (y+1) CW), CW = merge_cols (chosen by the plan:
+// few columns per workgroup when segments have many pieces, up to the NG =
+// 256 / (D/4) columns its NG groups of D/4 threads cover).  With C columns
+// here (rounded up to a power of two), GPC = NG / C groups share a column, each
 // merging the pieces k = phase, phase + GPC, ... online (four loads in
 // flight), and the groups of a column are combined through LDS in phase
 // order.  The result depends only on the pieces, not on timing.  Segments
@@ -1546,7 +1546,7 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(StreamParams
   const int slot0 = sj.x;
   const int nparts = sj.y;
   if (nparts <= 1) return;  // written whole by the attention kernel
-  const int cw = (gridDim.y == 1) ? p.cols_per_block : (p.cols_per_block <= 4 ? 1 : NG);
+  const int cw = p.merge_cols;
   const int cy0 = blockIdx.y * cw;
   const int cols_here = min(cw, min(p.cols_per_block, G * Q - col0) - cy0);
   if (cols_here <= 0) return;
@@ -1684,17 +1684,25 @@ hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int 
   return hipLaunchKernel(f, dim3(grid), dim3(64 * waves_per_group(v)), args, 0, stream);
 }
 
-// One workgroup per (segment, column) for blocks of at most 4 columns,
-// per (segment, 256 / (D/4) columns) otherwise.
-int merge_grid_y(const Variant& v, int cols_per_block) {
-  if (cols_per_block <= 4) return cols_per_block;
-  const int cw = kMergeThreads / (v.head_dim / 4);
-  return (cols_per_block + cw - 1) / cw;
+// Columns per merge workgroup: one for blocks of at most 4 columns (decode)
+// and when segments have many pieces (expected_parts per segment: a
+// column's pieces then spread over up to NG / C thread groups), else as
+// many as the NG = 256 / (D/4) thread groups cover.
+int merge_cols_for(const Variant& v, int cols_per_block, int64_t expected_parts) {
+  if (cols_per_block <= 4) return 1;
+  const int ng = kMergeThreads / (v.head_dim / 4);
+  int spread = 1;
+  while (spread < expected_parts && spread < ng) spread <<= 1;
+  return ng / spread;
+}
+
+int merge_grid_y(int cols_per_block, int merge_cols) {
+  return (cols_per_block + merge_cols - 1) / merge_cols;
 }
 
 hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  const dim3 g(grid, merge_grid_y(v, p.cols_per_block));
+  const dim3 g(grid, merge_grid_y(p.cols_per_block, p.merge_cols));
   const dim3 block(kMergeThreads);
   if (v.head_dim == 128) {
     if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<128, true>), g, block, 0, stream, p);

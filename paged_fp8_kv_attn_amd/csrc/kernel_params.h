@@ -31,6 +31,7 @@ struct StreamParams {
   int32_t max_q_len;
   int32_t cols_per_block;      // query columns (new token x head of a group) per workgroup
   int32_t col_blocks;          // column blocks of one (sequence, kv head)
+  int32_t merge_cols;          // query columns per merge workgroup
   int32_t unit_min_chunks;     // units in use: total chunks / this, within [1, max_units]
   int32_t max_units;           // units sharing the chunks at most (waves or workgroups)
   int64_t v_scale_offset;      // P * Hkv: start of the V scales in kv_scales
@@ -70,7 +71,8 @@ hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int 
 hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu);
 // Merge kernel: `grid` = segments workgroups along x, merge_grid_y along y.
 hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream);
-int merge_grid_y(const Variant& v, int cols_per_block);
+int merge_cols_for(const Variant& v, int cols_per_block, int64_t expected_parts);
+int merge_grid_y(int cols_per_block, int merge_cols);
 
 struct GatherParams {
   const uint8_t* k_pages;
