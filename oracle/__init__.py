@@ -23,3 +23,4 @@ library attention routine, closed forms and invariants); none is
 
 from .e4m3 import decode, decode_table  # noqa: F401
 from .attention import gather_sequence, paged_attention  # noqa: F401
+from .kv_append import encode as encode_e4m3, kv_append as paged_kv_append  # noqa: F401

@@ -117,3 +117,65 @@ def sdpa_attention(w) -> np.ndarray:
         out[row : row + Q] = o.permute(1, 0, 2)
         row += Q
     return out.numpy()
+
+
+def e4m3_encode_brute(y: float) -> int:
+    """Nearest finite E4M3 code to fp32 y by trying all 127 magnitudes (ties
+    to the code with mantissa bit 0 clear), magnitude clipped to 448, sign
+    bit from y's sign bit."""
+    mag = min(abs(y), 448.0)
+    best, best_d = 0, None
+    for c in range(0x7F):
+        d = abs(e4m3_by_bits(c) - mag)
+        if best_d is None or d < best_d or (d == best_d and (c & 1) == 0 and (best & 1) == 1):
+            best, best_d = c, d
+    return best | (0x80 if math.copysign(1.0, y) < 0 else 0)
+
+
+def _f32(x: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def brute_force_append(c):
+    """Pure-Python loops over flat byte offsets: quantise an AppendCase's new
+    rows into copies of its pools (tiny cases only)."""
+    S, D, Hkv = 16, c.head_dim, c.num_kv_heads
+    kflat = c.k_pages.reshape(-1).copy()
+    vflat = c.v_pages.reshape(-1).copy()
+    scales = c.kv_scales.copy()
+    kn = c.k_new.float().numpy()
+    vn = c.v_new.float().numpy()
+    nvb = D // 16
+
+    def k_off(p, h, s, d):
+        return (((p * Hkv + h) * (D // 16) + d // 16) * S + s) * 16 + d % 16
+
+    def v_off(p, h, s, d):
+        a, i, e = d // nvb, (d % nvb) // 4, d % 4
+        return (((((p * Hkv + h) * (S // 4) + s // 4) * (D // 64) + i) * 16 + a) * 4 + e) * 4 + s % 4
+
+    row = 0
+    for b in range(c.num_seqs):
+        L, Q = int(c.ctx_lens[b]), int(c.q_lens[b])
+        for t0 in range(((L - Q) // S) * S, L, S):  # first slot of each touched page
+            p = int(c.block_table[b][t0 // S])
+            for h in range(Hkv):
+                for which, flat, new, off in ((0, kflat, kn, k_off), (1, vflat, vn, v_off)):
+                    old_scale = float(scales[which][p, h])
+                    vals = {}
+                    for s in range(S):
+                        t = t0 + s
+                        if t >= L:
+                            break
+                        for d in range(D):
+                            if t < L - Q:
+                                vals[(s, d)] = _f32(e4m3_by_bits(int(flat[off(p, h, s, d)])) * old_scale)
+                            else:
+                                vals[(s, d)] = float(new[row + t - (L - Q), h, d])
+                    amax = max(abs(x) for x in vals.values())
+                    sc = 1.0 if amax == 0 else _f32(amax / 448.0)
+                    scales[which][p, h] = sc
+                    for (s, d), x in vals.items():
+                        flat[off(p, h, s, d)] = e4m3_encode_brute(_f32(x / sc))
+        row += Q
+    return kflat.reshape(c.k_pages.shape), vflat.reshape(c.v_pages.shape), scales
