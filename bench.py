@@ -45,6 +45,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATION_BYTES = 1 << 30
 KERNEL_SOURCE = os.path.join(ROOT, "paged_fp8_kv_attn_amd", "csrc", "attn_stream.hip")
+APPEND_SOURCE = os.path.join(ROOT, "paged_fp8_kv_attn_amd", "csrc", "attn_append.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 # workloads made of several forwards per step, enqueued back to back on one
 # stream: the chunked-prefill chunk and the MQA decode batch of one serving
@@ -71,6 +72,75 @@ def algorithmic_counts(w) -> dict:
                 query_tokens=int(Q.sum()))
 
 
+APPEND_WORKLOADS = ("append_decode", "append_prefill")
+
+
+def append_counts(c) -> dict:
+    """Bytes the append itself must move: the new rows read, their bytes
+    written, the cached bytes of every touched page read (the page absmax
+    covers them), the touched pages' scales read and written, their
+    block-table entries and the lengths."""
+    S = 16
+    elt = 4 if c.new_dtype == "f32" else 2
+    L = c.ctx_lens.astype(np.int64)
+    Q = c.q_lens.astype(np.int64)
+    n0 = L - Q
+    touched = (L - 1) // S - n0 // S + 1
+    cached_in_touched = n0 - (n0 // S) * S  # cached slots of the first touched page
+    hd = c.num_kv_heads * c.head_dim
+    rows = int(Q.sum()) * hd * 2 * elt
+    written = int(Q.sum()) * hd * 2
+    cached = int(cached_in_touched.sum()) * hd * 2
+    scales = int(touched.sum()) * c.num_kv_heads * 2 * 8
+    bt = int(touched.sum()) * 4
+    return dict(bytes=rows + written + cached + scales + bt + 8 * c.num_seqs, kv_bytes=written, flops=0, pairs=0,
+                query_tokens=int(Q.sum()))
+
+
+def append_config(c) -> dict:
+    return {
+        "workload": c.name,
+        "batch": c.num_seqs,
+        "kv_heads": c.num_kv_heads,
+        "head_dim": c.head_dim,
+        "page_size": 16,
+        "new_tokens": sorted(set(int(x) for x in c.q_lens))[:4],
+        "ctx_min": int(c.ctx_lens.min()),
+        "ctx_max": int(c.ctx_lens.max()),
+        "new_dtype": c.new_dtype,
+        "kv_format": "fp8_e4m3 (OCP), fp32 scale per (page, kv head)",
+        "seed": c.seed,
+    }
+
+
+def append_cpu_baseline(c, counts, budget_s: float) -> dict:
+    """Time the append oracle (as it stands) on the host over whole calls."""
+    import oracle
+
+    ncpu = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    calls = 0
+    while True:
+        oracle.paged_kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.kv_scales, c.block_table, c.ctx_lens,
+                               c.q_lens)
+        calls += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    return {
+        "value": counts["bytes"] * calls / wall / 1e9,
+        "unit": "GB/s",
+        "cores": max(1, int(math.ceil(cpu / wall - 0.05))),
+        "kind": "oracle",
+        "sample": (f"{calls} whole append calls of the same workload (copying the pools each call), {wall:.1f} s "
+                   f"wall, {cpu:.1f} s CPU on {ncpu} allowed threads; numpy oracle"),
+        "threads_allowed": ncpu,
+    }
+
+
 def workload_config(w) -> dict:
     return {
         "workload": w.name,
@@ -90,10 +160,10 @@ def workload_config(w) -> dict:
     }
 
 
-def source_hash() -> str:
-    """Hash of the attention kernel's source, so a counter summary taken on an
-    older kernel is not applied to a newer one."""
-    with open(KERNEL_SOURCE, "rb") as f:
+def source_hash(path: str = KERNEL_SOURCE) -> str:
+    """Hash of a kernel's source, so a counter summary taken on an older
+    kernel is not applied to a newer one."""
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -121,7 +191,8 @@ def committed_traffic(workload: str, kernel: str = "attn_stream_kernel"):
             if ":" in line and not line.lstrip().startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != source_hash():
+    src = APPEND_SOURCE if kernel == "kv_append_kernel" else KERNEL_SOURCE
+    if vals.get("kernel_source_sha256_16") != source_hash(src):
         return None
     try:
         fetch = float(vals["attn_FETCH_SIZE_KiB_per_dispatch"])
@@ -329,7 +400,39 @@ def main():
             k, v, s_ = self.pools[i % self.copies]
             self.plan.forward(self.q, k, v, s_, self.bt, self.ctx, self.ql, self.out, stream=st)
 
-    parts = [Part(n) for n in names]
+    class AppendPart:
+        """One append call per step (attn_kv_append) on a rotation of pool
+        copies of >= 1 GiB; the same rows are appended at the same positions
+        every time a copy comes round."""
+
+        def __init__(self, name):
+            from synth.append import make_append_case
+
+            c = make_append_case(name)
+            self.w = c
+            self.counts = append_counts(c)
+            self.plan = Plan(num_seqs=c.num_seqs, num_q_heads=c.num_kv_heads, num_kv_heads=c.num_kv_heads,
+                             head_dim=c.head_dim, num_pages=c.num_pages, max_pages_per_seq=c.max_pages_per_seq,
+                             max_q_len=c.max_q_len, max_ctx_len=c.max_ctx_len)
+            self.k_new = c.k_new.to(dev).contiguous()
+            self.v_new = c.v_new.to(dev).contiguous()
+            self.bt = t(c.block_table)
+            self.ctx = t(c.ctx_lens)
+            self.ql = t(c.q_lens)
+            k0, v0, s0 = t(c.k_pages), t(c.v_pages), t(c.kv_scales)
+            pool_bytes = k0.numel() + v0.numel() + s0.numel() * 4
+            self.copies = max(2, math.ceil(ROTATION_BYTES / pool_bytes))
+            self.pools = [(k0, v0, s0)] + [(k0.clone(), v0.clone(), s0.clone()) for _ in range(self.copies - 1)]
+            self.kernel = "kv_append_kernel"
+
+        def forward(self, i, st):
+            k, v, s_ = self.pools[i % self.copies]
+            self.plan.kv_append(self.k_new, self.v_new, k, v, s_, self.bt, self.ctx, self.ql, stream=st)
+
+    if args.workload in APPEND_WORKLOADS:
+        parts = [AppendPart(args.workload)]
+    else:
+        parts = [Part(n) for n in names]
     counts = {key: sum(pt.counts[key] for pt in parts) for key in parts[0].counts}
 
     def fwd(i, st=stream):
@@ -427,7 +530,9 @@ def main():
     gbs = counts["bytes"] / (ms * 1e-3) / 1e9
     tflops = counts["flops"] / (ms * 1e-3) / 1e12
     qtok = counts["query_tokens"] / (ms * 1e-3)
-    if len(parts) == 1:
+    if args.workload in APPEND_WORKLOADS:
+        config = append_config(parts[0].w)
+    elif len(parts) == 1:
         config = workload_config(parts[0].w)
     else:
         config = {"workload": args.workload, "parts": [workload_config(pt.w) for pt in parts],
@@ -452,14 +557,18 @@ def main():
         "launch": "graph" if graph is not None else "eager",
         "kv_pool_copies": [pt.copies for pt in parts] if len(parts) > 1 else parts[0].copies,
         "plan": [pt.plan.info() for pt in parts] if len(parts) > 1 else parts[0].plan.info(),
-        "kernel_source_sha256_16": source_hash(),
+        "kernel_source_sha256_16": source_hash(APPEND_SOURCE if args.workload in APPEND_WORKLOADS else KERNEL_SOURCE),
         "roofline": roof,
         "cpu_baseline": None,
     }
     if len(parts) > 1:
         res["parts"] = [{"workload": pt.w.name, "roofline": roofline(pt, committed_traffic(pt.w.name, pt.kernel))}
                         for pt in parts]
-    if not args.no_cpu_baseline:
+    if args.workload in APPEND_WORKLOADS:
+        res["dtype"] = "f32 (IEEE divide) -> fp8 e4m3"
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = append_cpu_baseline(dom.w, dom.counts, args.cpu_seconds)
+    elif not args.no_cpu_baseline:
         # the oracle on the first part (the dominant one for the mixed workload)
         res["cpu_baseline"] = cpu_baseline(dom.w, dom.counts, args.cpu_seconds)
         if len(parts) > 1:

@@ -164,14 +164,53 @@ attn_status_t attn_plan_destroy(attn_plan_t plan);
 attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info);
 
 /* Measurement hook.  With both events non-null, every later forward on this
- * plan launches its attention kernel with `attention_start` and
- * `attention_stop` attached to the kernel's own dispatch (hipExtLaunchKernel),
+ * plan launches its attention kernel (and every attn_kv_append its append
+ * kernel) with `attention_start` and `attention_stop` attached to the
+ * kernel's own dispatch (hipExtLaunchKernel),
  * so hipEventElapsedTime gives that kernel's duration alone (the merge kernel
  * that may follow is not included).  Both null turns it off; exactly one null
  * is ATTN_ERR_INVALID_ARGUMENT.  The events stay owned by the caller and must
  * outlive their use; forwards under stream capture should not set them. */
 attn_status_t attn_plan_set_kernel_events(attn_plan_t plan, hipEvent_t attention_start,
                                           hipEvent_t attention_stop);
+
+/* ---- the step before the attention: appending new tokens' K/V ----------
+ * Follows the same passages as the attention (memory section: fixed-size
+ * blocks of a preallocated pool; quantisation section: FP8 with per-group
+ * scale factors; GB10 article: the paged FP8 KV cache that decode, MTP
+ * verification and prefill append to).
+ *
+ * For each sequence b the Q_b rows k_new[r_b + i], v_new[r_b + i] (i < Q_b,
+ * r_b = Q_0 + ... + Q_{b-1}) become keys L_b - Q_b + i, stored through
+ * block_table[b] (so after the call L_b keys are cached, as the forward
+ * expects).  For every (page, kv head) the append touches, separately for K
+ * and V:
+ *   value(slot) = decoded byte * old scale     for the L_b - Q_b cached keys
+ *               = the new row's value           for the new keys
+ *   scale       = fp32(max |value| over the page's keys < L_b) / 448,
+ *                 1 if that maximum is 0
+ *   byte(slot)  = nearest E4M3 code to fp32(value / scale), ties to even,
+ *                 magnitudes above 448 saturated, sign kept
+ * for every slot holding a key < L_b (cached keys are encoded again, and
+ * keep their bytes exactly when the scale does not change); slots >= L_b and
+ * pages the append does not touch keep their bytes.  The divisions and the
+ * product are IEEE fp32, so the bytes and scales are exactly determined.
+ *
+ *   k_new, v_new  [sum Q_b][Hkv][D], new_dtype BF16 or F32, 16-byte aligned,
+ *                 finite values
+ *   k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens: as for the
+ *                 forward (ctx_lens counts the appended tokens); k_pages and
+ *                 v_pages 16-byte aligned, the int32/fp32 arrays 4-byte aligned.
+ * Preconditions beyond the forward's: block_table[b][j] in [0, P) for the
+ * pages j = (L_b - Q_b)/16 .. (L_b - 1)/16; no two sequences touch the same
+ * page (each is written by one wave).  Asynchronous on `stream`; allocates
+ * nothing; reads and writes only the pools and scales of the touched pages.
+ * The plan supplies the shape (B, Hkv, D, P, max_pages_per_seq, max_q_len);
+ * its kernel events, when set, are attached to this kernel's dispatch too. */
+attn_status_t attn_kv_append(attn_plan_t plan, const void* k_new, const void* v_new, attn_dtype_t new_dtype,
+                             uint8_t* k_pages, uint8_t* v_pages, float* kv_scales,
+                             const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                             hipStream_t stream);
 
 /* Static, never-null text for a status code. */
 const char* attn_status_string(attn_status_t status);
@@ -196,6 +235,11 @@ attn_status_t attn_debug_gather(attn_plan_t plan, const uint8_t* k_pages, const 
 /* out[i] = the value of E4M3 byte in[i] as the attention kernels decode it
  * (FP8 -> bf16, widened exactly to fp32).  n >= 0; n == 0 enqueues nothing. */
 attn_status_t attn_debug_decode_fp8(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
+
+/* out[i] = the E4M3 byte of fp32 in[i] as the append kernel encodes it
+ * (nearest code, ties to even, magnitudes above 448 saturated, sign kept;
+ * finite inputs).  n >= 0; n == 0 enqueues nothing. */
+attn_status_t attn_debug_encode_fp8(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 #ifdef __cplusplus
 }

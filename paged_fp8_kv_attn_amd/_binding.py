@@ -29,6 +29,8 @@ _FUNCTIONS = [
     "attn_last_hip_error",
     "attn_debug_gather",
     "attn_debug_decode_fp8",
+    "attn_kv_append",
+    "attn_debug_encode_fp8",
 ]
 
 
@@ -117,6 +119,10 @@ def load_library():
     lib.attn_debug_gather.restype = i32
     lib.attn_debug_decode_fp8.argtypes = [vp, vp, i64, vp]
     lib.attn_debug_decode_fp8.restype = i32
+    lib.attn_kv_append.argtypes = [vp, vp, vp, i32] + [vp] * 7
+    lib.attn_kv_append.restype = i32
+    lib.attn_debug_encode_fp8.argtypes = [vp, vp, i64, vp]
+    lib.attn_debug_encode_fp8.restype = i32
     _lib = lib
     return lib
 
@@ -211,6 +217,16 @@ class Plan:
         _check(st, "attn_paged_forward")
         return out
 
+    def kv_append(self, k_new, v_new, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, stream=None):
+        """Quantise the new rows k_new/v_new ([sum Q][Hkv][D], bf16 or fp32)
+        into the pools in place (attn_kv_append)."""
+        if k_new.dtype != v_new.dtype:
+            raise ValueError("k_new and v_new must have the same dtype")
+        st = load_library().attn_kv_append(
+            self._h, _ptr(k_new), _ptr(v_new), _dtype_code(k_new.dtype), _ptr(k_pages), _ptr(v_pages),
+            _ptr(kv_scales), _ptr(block_table), _ptr(ctx_lens), _ptr(q_lens), _stream(stream))
+        _check(st, "attn_kv_append")
+
     def close(self):
         if self._h:
             _check(load_library().attn_plan_destroy(self._h), "attn_plan_destroy")
@@ -234,4 +250,10 @@ def debug_gather(plan: Plan, k_pages, v_pages, kv_scales, block_table, ctx_lens,
 def debug_decode_fp8(codes, out, stream=None):
     st = load_library().attn_debug_decode_fp8(_ptr(codes), _ptr(out), int(codes.numel()), _stream(stream))
     _check(st, "attn_debug_decode_fp8")
+    return out
+
+
+def debug_encode_fp8(values, out, stream=None):
+    st = load_library().attn_debug_encode_fp8(_ptr(values), _ptr(out), int(values.numel()), _stream(stream))
+    _check(st, "attn_debug_encode_fp8")
     return out

@@ -382,6 +382,46 @@ attn_status_t attn_debug_gather(attn_plan_t plan, const uint8_t* k_pages, const 
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+attn_status_t attn_kv_append(attn_plan_t plan, const void* k_new, const void* v_new, attn_dtype_t new_dtype,
+                             uint8_t* k_pages, uint8_t* v_pages, float* kv_scales, const int32_t* block_table,
+                             const int32_t* ctx_lens, const int32_t* q_lens, hipStream_t stream) {
+  if (!plan || !k_new || !v_new || !k_pages || !v_pages || !kv_scales || !block_table || !ctx_lens || !q_lens)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (new_dtype != ATTN_DTYPE_F32 && new_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+      !aligned(kv_scales, 4) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) || !aligned(q_lens, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  const attn_status_t dst = check_device(plan);
+  if (dst != ATTN_OK) return dst;
+  const attn_plan_desc_t& d = plan->desc;
+  pa::AppendParams ap{};
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.k_pages = k_pages;
+  ap.v_pages = v_pages;
+  ap.kv_scales = kv_scales;
+  ap.block_table = block_table;
+  ap.ctx_lens = ctx_lens;
+  ap.q_lens = q_lens;
+  ap.num_seqs = d.num_seqs;
+  ap.num_kv_heads = d.num_kv_heads;
+  ap.bt_stride = d.max_pages_per_seq;
+  // Q new keys starting anywhere in a page span at most ceil(Q/16) + 1 pages
+  ap.max_touch = std::min<int>(ceil_div(d.max_q_len, pa::kPageSize) + 1, d.max_pages_per_seq);
+  ap.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
+  const hipError_t e = pa::launch_kv_append(ap, d.head_dim, new_dtype == ATTN_DTYPE_F32, stream, plan->ev_start,
+                                            plan->ev_stop);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+attn_status_t attn_debug_encode_fp8(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (n < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (n == 0) return ATTN_OK;
+  if (!in || !out || !aligned(in, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  const hipError_t e = pa::launch_debug_encode(in, out, n, stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
 attn_status_t attn_debug_decode_fp8(const uint8_t* in, float* out, int64_t n, hipStream_t stream) {
   if (n < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (n == 0) return ATTN_OK;

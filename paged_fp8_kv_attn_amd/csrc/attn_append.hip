@@ -1,0 +1,245 @@
+// Paged FP8 KV append for gfx950: the new tokens' K and V rows of each
+// sequence are quantised into its pages through the block table, with one
+// fp32 scale per (page, kv head).
+//
+// Follows the memory section of the Atlas engine article (ainews.cool,
+// "技术深度解析": fixed-size KV blocks from a preallocated pool), its
+// quantisation section (FP8 with per-group scale factors) and the paged FP8
+// KV cache of the GB10 article (ainews.surl.tw).  Per touched (page, head):
+//   scale = fp32(max |value| over the page's valid slots) / 448 (1 if 0),
+// where cached slots count as decoded byte * old scale; every valid slot is
+// encoded as the nearest E4M3 code of fp32(value / scale) (ties to even,
+// saturated at 448); slots past the new length keep their bytes.
+//
+// One wave per (sequence, touched page, kv head, K or V).  A (page, head)
+// chunk is 16 * D bytes in the pool's layout; lane l owns its 16-byte units
+// D/64 * l .. +D/64-1, so the wave's stores cover the chunk in whole lines.
+// A unit is loaded only if it holds a slot that is cached or stays
+// untouched, and stored only if it holds a new slot or a cached one whose
+// scale changed (re-encoding with an unchanged scale reproduces the bytes).
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "kernel_params.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kAppendWaves = 4;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// n consecutive new values (n = 16 or 4) of one row, from d0.
+template <bool F32IN, int N>
+__device__ __forceinline__ void load_row(const void* base, int64_t off, float* v) {
+  if constexpr (F32IN) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const u32x4 w = src[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * k + e] = __uint_as_float(w[e]);
+    }
+  } else {
+    const uint16_t* src = static_cast<const uint16_t*>(base) + off;
+    if constexpr (N == 16) {
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const u32x4 w = s4[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[8 * k + 2 * e] = __uint_as_float(w[e] << 16);
+          v[8 * k + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      }
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(src);
+      v[0] = __uint_as_float(w.x << 16);
+      v[1] = __uint_as_float(w.x & 0xffff0000u);
+      v[2] = __uint_as_float(w.y << 16);
+      v[3] = __uint_as_float(w.y & 0xffff0000u);
+    }
+  }
+}
+
+template <int D, bool F32IN>
+__global__ __launch_bounds__(64 * kAppendWaves) void kv_append_kernel(AppendParams p) {
+  constexpr int U = D / 64;     // 16-byte units per lane
+  constexpr int NVB = D / 16;   // V: values of d per 16-row block
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  const int job = (int)blockIdx.x * kAppendWaves + wave;
+  const int per_page = 2 * p.num_kv_heads;
+  const int pi_local = job / per_page;
+  const int rem = job - pi_local * per_page;
+  const int h = rem >> 1;
+  const bool is_v = (rem & 1) != 0;
+  if (pi_local >= p.max_touch) return;
+  const int L = p.ctx_lens[b];
+  const int Q = p.q_lens[b];
+  const int n0 = L - Q;                      // keys cached before the append
+  const int pi = n0 / kPageSize + pi_local;  // page index inside the sequence
+  if (pi * kPageSize >= L) return;
+  int row0 = 0;  // first new row of sequence b
+  for (int base = 0; base < b; base += 64) {
+    const int i = base + lane;
+    row0 += wave_sum(i < b ? p.q_lens[i] : 0);
+  }
+  const int32_t page = p.block_table[(int64_t)b * p.bt_stride + pi];
+  const int valid = min(kPageSize, L - pi * kPageSize);
+  const int n_old = max(0, min(kPageSize, n0 - pi * kPageSize));
+  float* scale_at = p.kv_scales + (is_v ? p.v_scale_offset : 0) + (int64_t)page * p.num_kv_heads + h;
+  const float old_scale = n_old > 0 ? *scale_at : 0.f;
+  uint8_t* chunk = (is_v ? p.v_pages : p.k_pages) + chunk_offset(page, h, p.num_kv_heads, D);
+  const void* rows = is_v ? p.v_new : p.k_new;
+  const int64_t row_stride = (int64_t)p.num_kv_heads * D;
+
+  // element k of unit u: slot and d
+  auto slot_of = [&](int j, int k) -> int {
+    if (!is_v) return j % 16;
+    return 4 * (j / (D / 4)) + (k & 3);
+  };
+  float val[U][16];
+  u32x4 oldw[U];
+  float amax = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = U * lane + u;  // unit index inside the chunk
+    // slot range of the unit: one slot (K) or four consecutive ones (V)
+    const int s_lo = is_v ? 4 * (j / (D / 4)) : j % 16;
+    const int s_hi = is_v ? s_lo + 3 : s_lo;
+    const bool need_old = s_lo < n_old || s_hi >= valid;
+    oldw[u] = need_old ? *reinterpret_cast<const u32x4*>(chunk + 16 * j) : u32x4{0u, 0u, 0u, 0u};
+    float dec[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 f = fp8x4_to_f32x4(oldw[u][q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dec[4 * q + e] = f[e];
+    }
+    if (!is_v) {
+      // K unit: slot j % 16, d = 16 (j / 16) + k (byte k of the unit)
+      const int s = j % 16;
+      if (s >= n_old && s < valid) {
+        const int64_t r = row0 + (pi * kPageSize + s - n0);
+        load_row<F32IN, 16>(rows, r * row_stride + (int64_t)h * D + 16 * (j / 16), val[u]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) val[u][k] = dec[k] * old_scale;
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (s < valid) amax = fmaxf(amax, fabsf(val[u][k]));
+    } else {
+      // V unit: a = j % 16, i = (j / 16) % (D / 64), slots 4 (j / (D / 4)) + r;
+      // byte 4 e + r holds d = NVB a + 4 i + e of slot 4 sg + r
+      const int a = j % 16;
+      const int i = (j / 16) % (D / 64);
+      const int d0 = NVB * a + 4 * i;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = s_lo + r;
+        float nv[4];
+        if (s >= n_old && s < valid) {
+          const int64_t rr = row0 + (pi * kPageSize + s - n0);
+          load_row<F32IN, 4>(rows, rr * row_stride + (int64_t)h * D + d0, nv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nv[e] = dec[4 * e + r] * old_scale;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          val[u][4 * e + r] = nv[e];
+          if (s < valid) amax = fmaxf(amax, fabsf(nv[e]));
+        }
+      }
+    }
+  }
+  amax = wave_max(amax);
+  const float scale = (amax == 0.f) ? 1.f : amax / 448.f;
+  const bool changed = n_old == 0 || __float_as_uint(scale) != __float_as_uint(old_scale);
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = U * lane + u;
+    const int s_lo = is_v ? 4 * (j / (D / 4)) : j % 16;
+    const int s_hi = is_v ? s_lo + 3 : s_lo;
+    const bool has_new = s_hi >= n_old && s_lo < valid;
+    const bool has_old = s_lo < n_old;
+    if (!(has_new || (changed && has_old))) continue;
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = val[u][4 * q + e] / scale;
+      const uint32_t enc = f32x4_to_fp8x4(y[0], y[1], y[2], y[3]);
+      // bytes of slots at or past the new length keep their old value
+      uint32_t keep = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (slot_of(j, 4 * q + e) >= valid) keep |= 0xffu << (8 * e);
+      w[q] = (enc & ~keep) | (oldw[u][q] & keep);
+    }
+    *reinterpret_cast<u32x4*>(chunk + 16 * j) = w;
+  }
+  if (lane == 0) *scale_at = scale;
+}
+
+// one thread per 4 values
+__global__ __launch_bounds__(256) void debug_encode_kernel(const float* in, uint8_t* out, int64_t n) {
+  const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i0 >= n) return;
+  float x[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < 4 && i0 + k < n; ++k) x[k] = in[i0 + k];
+  const uint32_t w = f32x4_to_fp8x4(x[0], x[1], x[2], x[3]);
+  for (int k = 0; k < 4 && i0 + k < n; ++k) out[i0 + k] = (uint8_t)(w >> (8 * k));
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool new_f32, hipStream_t stream,
+                            hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const int64_t jobs = (int64_t)p.max_touch * 2 * p.num_kv_heads;
+  const int64_t gx = (jobs + kAppendWaves - 1) / kAppendWaves;
+  if (gx <= 0 || p.num_seqs <= 0) return hipSuccess;
+  if (gx > 0x7fffffff || p.num_seqs > 65535) return hipErrorInvalidValue;
+  const void* fn;
+  if (head_dim == 128)
+    fn = new_f32 ? reinterpret_cast<const void*>(&kv_append_kernel<128, true>)
+                 : reinterpret_cast<const void*>(&kv_append_kernel<128, false>);
+  else
+    fn = new_f32 ? reinterpret_cast<const void*>(&kv_append_kernel<64, true>)
+                 : reinterpret_cast<const void*>(&kv_append_kernel<64, false>);
+  AppendParams copy = p;
+  void* args[] = {&copy};
+  return hipExtLaunchKernel(fn, dim3((unsigned)gx, (unsigned)p.num_seqs), dim3(64 * kAppendWaves), args, 0, stream,
+                            ev_start, ev_stop, 0);
+}
+
+hipError_t launch_debug_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t threads = (n + 3) / 4;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(debug_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace pa

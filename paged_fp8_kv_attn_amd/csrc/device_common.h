@@ -60,6 +60,24 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Four fp32 -> four OCP E4M3 bytes (a in byte 0 .. d in byte 3), round to
+// nearest even.  Magnitudes above 448 are clamped first, since the converter
+// gives the NaN code for values past the largest finite one; -0 keeps its
+// sign.  Inputs are finite.
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
+  auto sat = [](float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.f), 448.f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
+}
+
+// Four FP8 E4M3 bytes -> four fp32 values, exactly.
+__device__ __forceinline__ f32x4 fp8x4_to_f32x4(uint32_t w) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -92,6 +92,28 @@ struct GatherParams {
   int64_t v_scale_offset;
 };
 
+// Paged FP8 KV append: the q_lens[b] new rows of each sequence become keys
+// ctx_lens[b] - q_lens[b] .. ctx_lens[b] - 1 of its pages.
+struct AppendParams {
+  const void* k_new;           // [sum Q][Hkv][D] bf16 or fp32
+  const void* v_new;
+  uint8_t* k_pages;            // [P][Hkv][D/16][16][16]
+  uint8_t* v_pages;            // [P][Hkv][4][D/64][16][4][4]
+  float* kv_scales;            // [2][P][Hkv]
+  const int32_t* block_table;  // [B][bt_stride]
+  const int32_t* ctx_lens;     // [B] after the append
+  const int32_t* q_lens;       // [B] rows appended
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t bt_stride;
+  int32_t max_touch;           // pages one sequence's append touches at most
+  int64_t v_scale_offset;      // P * Hkv
+};
+
+hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool new_f32, hipStream_t stream,
+                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+hipError_t launch_debug_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
 hipError_t launch_debug_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
 
