@@ -13,10 +13,13 @@
 //
 // One wave per (sequence, touched page, kv head, K or V).  A (page, head)
 // chunk is 16 * D bytes in the pool's layout; lane l owns its 16-byte units
-// D/64 * l .. +D/64-1, so the wave's stores cover the chunk in whole lines.
-// A unit is loaded only if it holds a slot that is cached or stays
-// untouched, and stored only if it holds a new slot or a cached one whose
-// scale changed (re-encoding with an unchanged scale reproduces the bytes).
+// (K: units D/64 * l ..; V at D = 128: the two units of one slot group and
+// 16-row block, so each slot's 8 new values are one 16-byte bf16 load), and
+// the wave's stores cover the chunk in whole lines.
+// New rows are read before anything that waits for the block table.  A unit
+// is loaded only if it holds a cached slot or an untouched slot beside a new
+// one, and stored only if it holds a new slot or a cached one whose scale
+// changed (re-encoding with an unchanged scale reproduces the bytes).
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -43,7 +46,7 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
-// n consecutive new values (n = 16 or 4) of one row, from d0.
+// N consecutive new values (N = 16, 8 or 4) of one row.
 template <bool F32IN, int N>
 __device__ __forceinline__ void load_row(const void* base, int64_t off, float* v) {
   if constexpr (F32IN) {
@@ -56,10 +59,10 @@ __device__ __forceinline__ void load_row(const void* base, int64_t off, float* v
     }
   } else {
     const uint16_t* src = static_cast<const uint16_t*>(base) + off;
-    if constexpr (N == 16) {
+    if constexpr (N == 16 || N == 8) {
       const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < N / 8; ++k) {
         const u32x4 w = s4[k];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -110,64 +113,86 @@ __global__ __launch_bounds__(64 * kAppendWaves) void kv_append_kernel(AppendPara
   const void* rows = is_v ? p.v_new : p.k_new;
   const int64_t row_stride = (int64_t)p.num_kv_heads * D;
 
-  // element k of unit u: slot and d
-  auto slot_of = [&](int j, int k) -> int {
-    if (!is_v) return j % 16;
-    return 4 * (j / (D / 4)) + (k & 3);
+  // Unit u of lane l.  K: unit j = U l + u holds slot j % 16, d = 16 (j / 16)
+  // + k at byte k.  V: with D = 128 the lane takes the two units of one
+  // (slot group sg, a) with i = 0, 1, so that for each of its 4 slots the 8
+  // values d = 8 a .. 8 a + 7 are consecutive in the new row; byte 4 e + r of
+  // unit (sg, i, a) holds d = NVB a + 4 i + e of slot 4 sg + r.
+  auto unit_of = [&](int u) -> int {
+    if (is_v && D == 128) return ((lane >> 4) * 2 + u) * 16 + (lane & 15);
+    return U * lane + u;
   };
-  float val[U][16];
+  auto slot_lo = [&](int j) -> int { return is_v ? 4 * (j / (D / 4)) : j % 16; };
+  auto slot_of = [&](int j, int k) -> int { return is_v ? slot_lo(j) + (k & 3) : j % 16; };
+  float val[U][16];  // untouched slots keep 0 here (their bytes are restored)
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) val[u][k] = 0.f;
   u32x4 oldw[U];
-  float amax = 0.f;
+  // new rows first: their addresses do not wait for the block table
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int j = U * lane + u;  // unit index inside the chunk
-    // slot range of the unit: one slot (K) or four consecutive ones (V)
-    const int s_lo = is_v ? 4 * (j / (D / 4)) : j % 16;
-    const int s_hi = is_v ? s_lo + 3 : s_lo;
-    const bool need_old = s_lo < n_old || s_hi >= valid;
-    oldw[u] = need_old ? *reinterpret_cast<const u32x4*>(chunk + 16 * j) : u32x4{0u, 0u, 0u, 0u};
-    float dec[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 f = fp8x4_to_f32x4(oldw[u][q]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dec[4 * q + e] = f[e];
-    }
+    const int j = unit_of(u);
     if (!is_v) {
-      // K unit: slot j % 16, d = 16 (j / 16) + k (byte k of the unit)
       const int s = j % 16;
       if (s >= n_old && s < valid) {
         const int64_t r = row0 + (pi * kPageSize + s - n0);
         load_row<F32IN, 16>(rows, r * row_stride + (int64_t)h * D + 16 * (j / 16), val[u]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) val[u][k] = dec[k] * old_scale;
       }
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (s < valid) amax = fmaxf(amax, fabsf(val[u][k]));
-    } else {
-      // V unit: a = j % 16, i = (j / 16) % (D / 64), slots 4 (j / (D / 4)) + r;
-      // byte 4 e + r holds d = NVB a + 4 i + e of slot 4 sg + r
-      const int a = j % 16;
-      const int i = (j / 16) % (D / 64);
-      const int d0 = NVB * a + 4 * i;
+    } else if (D != 128) {
+      const int d0 = NVB * (j % 16) + 4 * ((j / 16) % (D / 64));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int s = s_lo + r;
-        float nv[4];
+        const int s = slot_lo(j) + r;
         if (s >= n_old && s < valid) {
-          const int64_t rr = row0 + (pi * kPageSize + s - n0);
-          load_row<F32IN, 4>(rows, rr * row_stride + (int64_t)h * D + d0, nv);
-        } else {
+          float nv[4];
+          load_row<F32IN, 4>(rows, (row0 + (pi * kPageSize + s - n0)) * row_stride + (int64_t)h * D + d0, nv);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nv[e] = dec[4 * e + r] * old_scale;
+          for (int e = 0; e < 4; ++e) val[u][4 * e + r] = nv[e];
         }
+      }
+    }
+  }
+  if constexpr (D == 128) {
+    if (is_v) {
+      // both units of the lane: slots 4 sg + r, d = 8 a + 4 u + e
+      const int j0 = unit_of(0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          val[u][4 * e + r] = nv[e];
-          if (s < valid) amax = fmaxf(amax, fabsf(nv[e]));
+      for (int r = 0; r < 4; ++r) {
+        const int s = slot_lo(j0) + r;
+        if (s >= n_old && s < valid) {
+          float nv[8];
+          load_row<F32IN, 8>(rows, (row0 + (pi * kPageSize + s - n0)) * row_stride + (int64_t)h * D +
+                                       NVB * (lane & 15), nv);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[u][4 * e + r] = nv[4 * u + e];
         }
+      }
+    }
+  }
+  // cached and untouched bytes: a unit is read if it holds a cached slot, or
+  // an untouched slot next to a new one (its bytes are written back)
+  float amax = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = unit_of(u);
+    const int s_lo = slot_lo(j);
+    const int s_hi = is_v ? s_lo + 3 : s_lo;
+    const bool has_new = s_hi >= n_old && s_lo < valid;
+    const bool need_old = s_lo < n_old || (s_hi >= valid && has_new);
+    oldw[u] = need_old ? *reinterpret_cast<const u32x4*>(chunk + 16 * j) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 f = fp8x4_to_f32x4(oldw[u][q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * q + e;
+        const int s = slot_of(j, k);
+        if (s < n_old) val[u][k] = f[e] * old_scale;
+        if (s < valid) amax = fmaxf(amax, fabsf(val[u][k]));
       }
     }
   }
@@ -177,8 +202,8 @@ __global__ __launch_bounds__(64 * kAppendWaves) void kv_append_kernel(AppendPara
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int j = U * lane + u;
-    const int s_lo = is_v ? 4 * (j / (D / 4)) : j % 16;
+    const int j = unit_of(u);
+    const int s_lo = slot_lo(j);
     const int s_hi = is_v ? s_lo + 3 : s_lo;
     const bool has_new = s_hi >= n_old && s_lo < valid;
     const bool has_old = s_lo < n_old;
