@@ -13,6 +13,11 @@ What it follows:
     memory section (fixed-size preallocated KV blocks).
   * "Atlas Takes On vLLM ... on a Single GB10" (ainews.surl.tw): the paged
     FP8 KV cache and MTP with K=4 draft tokens (verification attention).
+Two neighbouring steps of the same serving path have their own plain
+statements: kv_append.py (new tokens' K/V quantised into the paged FP8
+pool, the step before the attention) and mtp_accept.py (greedy acceptance
+of the K = 4 drafts from the target's logits, the step after MTP
+verification; GB10 article: MTP with K = 4 under deterministic decoding).
 FlashAttention-2's tiled online softmax reaches, in exact arithmetic, plain
 softmax attention over the dequantised keys and values; so the oracle is that
 plain definition (see attention.py).  Every function is pinned by the
@@ -24,3 +29,4 @@ library attention routine, closed forms and invariants); none is
 from .e4m3 import decode, decode_table  # noqa: F401
 from .attention import gather_sequence, paged_attention  # noqa: F401
 from .kv_append import encode as encode_e4m3, kv_append as paged_kv_append  # noqa: F401
+from .mtp_accept import accept as greedy_accept, greedy_tokens  # noqa: F401
