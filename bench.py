@@ -46,6 +46,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATION_BYTES = 1 << 30
 KERNEL_SOURCE = os.path.join(ROOT, "paged_fp8_kv_attn_amd", "csrc", "attn_stream.hip")
 APPEND_SOURCE = os.path.join(ROOT, "paged_fp8_kv_attn_amd", "csrc", "attn_append.hip")
+ACCEPT_SOURCE = os.path.join(ROOT, "paged_fp8_kv_attn_amd", "csrc", "attn_accept.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 # workloads made of several forwards per step, enqueued back to back on one
 # stream: the chunked-prefill chunk and the MQA decode batch of one serving
@@ -141,6 +142,45 @@ def append_cpu_baseline(c, counts, budget_s: float) -> dict:
     }
 
 
+ACCEPT_WORKLOADS = ("mtp_accept",)
+
+
+def accept_counts(c) -> dict:
+    """Bytes greedy acceptance must move: the logits, the drafts, the target
+    tokens and accepted counts written."""
+    B, K, V = c.num_seqs, c.num_drafts, c.vocab
+    elt = c.logits.element_size()
+    return dict(bytes=B * (K + 1) * V * elt + B * K * 4 + B * (K + 1) * 4 + B * 4, kv_bytes=0, flops=0, pairs=0,
+                query_tokens=B * (K + 1))
+
+
+def accept_config(c) -> dict:
+    return {"workload": c.name, "batch": c.num_seqs, "drafts": c.num_drafts, "vocab": c.vocab,
+            "logits_dtype": str(c.logits.dtype).replace("torch.", ""), "seed": c.seed}
+
+
+def accept_cpu_baseline(c, counts, budget_s: float) -> dict:
+    """Time the acceptance oracle (as it stands) on the host over whole calls."""
+    import oracle
+
+    ncpu = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    calls = 0
+    while True:
+        oracle.greedy_accept(c.logits, c.drafts)
+        calls += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    return {"value": counts["bytes"] * calls / wall / 1e9, "unit": "GB/s",
+            "cores": max(1, int(math.ceil(cpu / wall - 0.05))), "kind": "oracle",
+            "sample": (f"{calls} whole acceptance calls of the same workload, {wall:.1f} s wall, {cpu:.1f} s CPU "
+                       f"on {ncpu} allowed threads; numpy oracle"), "threads_allowed": ncpu}
+
+
 def workload_config(w) -> dict:
     return {
         "workload": w.name,
@@ -191,7 +231,7 @@ def committed_traffic(workload: str, kernel: str = "attn_stream_kernel"):
             if ":" in line and not line.lstrip().startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    src = APPEND_SOURCE if kernel == "kv_append_kernel" else KERNEL_SOURCE
+    src = {"kv_append_kernel": APPEND_SOURCE, "argmax_partial_kernel": ACCEPT_SOURCE}.get(kernel, KERNEL_SOURCE)
     if vals.get("kernel_source_sha256_16") != source_hash(src):
         return None
     try:
@@ -429,8 +469,50 @@ def main():
             k, v, s_ = self.pools[i % self.copies]
             self.plan.kv_append(self.k_new, self.v_new, k, v, s_, self.bt, self.ctx, self.ql, stream=st)
 
+    class AcceptPart:
+        """One greedy acceptance call per step (attn_mtp_accept) on a
+        rotation of >= 1 GiB of logits copies."""
+
+        def __init__(self, name):
+            from paged_fp8_kv_attn_amd import mtp_accept, mtp_accept_workspace_size
+            from synth.accept import make_accept_case
+
+            c = make_accept_case(name)
+            self.w = c
+            self.counts = accept_counts(c)
+            self._accept = mtp_accept
+            B, K, V = c.num_seqs, c.num_drafts, c.vocab
+            l0 = c.logits.to(dev).contiguous()
+            self.copies = max(2, math.ceil(ROTATION_BYTES / (l0.numel() * l0.element_size())))
+            self.pools = [l0] + [l0.clone() for _ in range(self.copies - 1)]
+            self.drafts = t(c.drafts)
+            self.targets = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+            self.n = torch.empty((B,), dtype=torch.int32, device=dev)
+            self.ws = torch.empty(mtp_accept_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+            self.kernel = "argmax_partial_kernel"
+            self.events = None
+            outer = self
+
+            class _EvPlan:
+                def set_kernel_events(self, a, b):
+                    outer.events = None if a is None else (a, b)
+
+                def info(self):
+                    return {"segments_per_row": mtp_accept_workspace_size(B, K, V) // (8 * B * (K + 1))}
+
+                def close(self):
+                    pass
+
+            self.plan = _EvPlan()
+
+        def forward(self, i, st):
+            self._accept(self.pools[i % self.copies], self.drafts, self.targets, self.n, self.ws,
+                         kernel_events=self.events, stream=st)
+
     if args.workload in APPEND_WORKLOADS:
         parts = [AppendPart(args.workload)]
+    elif args.workload in ACCEPT_WORKLOADS:
+        parts = [AcceptPart(args.workload)]
     else:
         parts = [Part(n) for n in names]
     counts = {key: sum(pt.counts[key] for pt in parts) for key in parts[0].counts}
@@ -532,6 +614,8 @@ def main():
     qtok = counts["query_tokens"] / (ms * 1e-3)
     if args.workload in APPEND_WORKLOADS:
         config = append_config(parts[0].w)
+    elif args.workload in ACCEPT_WORKLOADS:
+        config = accept_config(parts[0].w)
     elif len(parts) == 1:
         config = workload_config(parts[0].w)
     else:
@@ -557,7 +641,8 @@ def main():
         "launch": "graph" if graph is not None else "eager",
         "kv_pool_copies": [pt.copies for pt in parts] if len(parts) > 1 else parts[0].copies,
         "plan": [pt.plan.info() for pt in parts] if len(parts) > 1 else parts[0].plan.info(),
-        "kernel_source_sha256_16": source_hash(APPEND_SOURCE if args.workload in APPEND_WORKLOADS else KERNEL_SOURCE),
+        "kernel_source_sha256_16": source_hash(APPEND_SOURCE if args.workload in APPEND_WORKLOADS else
+                                               ACCEPT_SOURCE if args.workload in ACCEPT_WORKLOADS else KERNEL_SOURCE),
         "roofline": roof,
         "cpu_baseline": None,
     }
@@ -568,6 +653,10 @@ def main():
         res["dtype"] = "f32 (IEEE divide) -> fp8 e4m3"
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = append_cpu_baseline(dom.w, dom.counts, args.cpu_seconds)
+    elif args.workload in ACCEPT_WORKLOADS:
+        res["dtype"] = "bf16 compare, int32 tokens"
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = accept_cpu_baseline(dom.w, dom.counts, args.cpu_seconds)
     elif not args.no_cpu_baseline:
         # the oracle on the first part (the dominant one for the mixed workload)
         res["cpu_baseline"] = cpu_baseline(dom.w, dom.counts, args.cpu_seconds)

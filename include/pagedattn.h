@@ -3,7 +3,9 @@
  *
  * One operation: attention of new query tokens over a KV cache that is kept
  * in fixed-size pages of a preallocated pool, stored as FP8 E4M3 bytes with
- * one fp32 scale per (page, kv head), with grouped/multi-query heads.
+ * one fp32 scale per (page, kv head), with grouped/multi-query heads; and
+ * the steps on either side of it: appending new tokens' K/V to the pool,
+ * and greedy acceptance of MTP drafts after verification.
  *
  * The operation follows these passages:
  *   - Atlas engine article (ainews.cool), section "技术深度解析":
@@ -211,6 +213,32 @@ attn_status_t attn_kv_append(attn_plan_t plan, const void* k_new, const void* v_
                              uint8_t* k_pages, uint8_t* v_pages, float* kv_scales,
                              const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
                              hipStream_t stream);
+
+/* ---- the step after MTP verification: greedy acceptance of the drafts ----
+ * The GB10 article serves with multi-token prediction, K = 4 drafts, under
+ * deterministic decoding.  For sequence b and position i <= K (row
+ * r = b (K+1) + i of the target model's logits):
+ *   target_tokens[r] = the lowest index v holding the largest logits[r][v]
+ *                      (+0 and -0 are equal; logits finite)
+ *   num_accepted[b]  = the largest n <= K with draft_tokens[b][j] ==
+ *                      target_tokens[b (K+1) + j] for every j < n
+ * (the tokens emitted are then target_tokens[b (K+1) + 0 .. n]).
+ *   logits         [B][K+1][vocab] BF16 or F32, 16-byte aligned; vocab a
+ *                  multiple of 8, at most 2^31 - 1
+ *   draft_tokens   int32 [B][K]; target_tokens int32 [B][K+1];
+ *   num_accepted   int32 [B]
+ *   workspace      device memory of attn_mtp_accept_workspace_size() bytes,
+ *                  8-byte aligned, owned by the caller (not kept)
+ *   kernel_start, kernel_stop  measurement hook: when both are non-null they
+ *                  are attached to the dispatch of the argmax kernel (the
+ *                  one that reads the logits); null for normal use.
+ * B (K+1) <= 65535.  Asynchronous on `stream`; allocates nothing.  Errors as
+ * elsewhere: bad arguments return before any launch. */
+size_t attn_mtp_accept_workspace_size(int32_t num_seqs, int32_t num_drafts, int32_t vocab);
+attn_status_t attn_mtp_accept(const void* logits, attn_dtype_t logits_dtype, const int32_t* draft_tokens,
+                              int32_t num_seqs, int32_t num_drafts, int32_t vocab, int32_t* target_tokens,
+                              int32_t* num_accepted, void* workspace, size_t workspace_bytes,
+                              hipEvent_t kernel_start, hipEvent_t kernel_stop, hipStream_t stream);
 
 /* Static, never-null text for a status code. */
 const char* attn_status_string(attn_status_t status);

@@ -15,5 +15,7 @@ from ._binding import (  # noqa: F401
     exported_symbols,
     library_path,
     load_library,
+    mtp_accept,
+    mtp_accept_workspace_size,
     status_string,
 )

@@ -31,6 +31,8 @@ _FUNCTIONS = [
     "attn_debug_decode_fp8",
     "attn_kv_append",
     "attn_debug_encode_fp8",
+    "attn_mtp_accept_workspace_size",
+    "attn_mtp_accept",
 ]
 
 
@@ -123,6 +125,10 @@ def load_library():
     lib.attn_kv_append.restype = i32
     lib.attn_debug_encode_fp8.argtypes = [vp, vp, i64, vp]
     lib.attn_debug_encode_fp8.restype = i32
+    lib.attn_mtp_accept_workspace_size.argtypes = [i32, i32, i32]
+    lib.attn_mtp_accept_workspace_size.restype = ctypes.c_size_t
+    lib.attn_mtp_accept.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp, vp, vp]
+    lib.attn_mtp_accept.restype = i32
     _lib = lib
     return lib
 
@@ -257,3 +263,22 @@ def debug_encode_fp8(values, out, stream=None):
     st = load_library().attn_debug_encode_fp8(_ptr(values), _ptr(out), int(values.numel()), _stream(stream))
     _check(st, "attn_debug_encode_fp8")
     return out
+
+
+def mtp_accept_workspace_size(num_seqs: int, num_drafts: int, vocab: int) -> int:
+    return int(load_library().attn_mtp_accept_workspace_size(num_seqs, num_drafts, vocab))
+
+
+def mtp_accept(logits, drafts, target_tokens, num_accepted, workspace, kernel_events=None, stream=None):
+    """Greedy acceptance (attn_mtp_accept): logits [B][K+1][V] bf16/fp32,
+    drafts int32 [B][K]; fills target_tokens int32 [B][K+1] and
+    num_accepted int32 [B].  workspace: a uint8 device tensor of at least
+    mtp_accept_workspace_size(B, K, V) bytes."""
+    B, K1, V = logits.shape
+    ev = (None, None) if kernel_events is None else tuple(ctypes.c_void_p(e) if isinstance(e, int) else e
+                                                        for e in kernel_events)
+    st = load_library().attn_mtp_accept(
+        _ptr(logits), _dtype_code(logits.dtype), _ptr(drafts), B, K1 - 1, V, _ptr(target_tokens),
+        _ptr(num_accepted), _ptr(workspace), workspace.numel() * workspace.element_size(), ev[0], ev[1],
+        _stream(stream))
+    _check(st, "attn_mtp_accept")

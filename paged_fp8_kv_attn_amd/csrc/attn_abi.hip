@@ -414,6 +414,41 @@ attn_status_t attn_kv_append(attn_plan_t plan, const void* k_new, const void* v_
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+size_t attn_mtp_accept_workspace_size(int32_t num_seqs, int32_t num_drafts, int32_t vocab) {
+  if (num_seqs < 1 || num_drafts < 0 || vocab < 8) return 0;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * (num_drafts + 1);
+  return static_cast<size_t>(rows) * pa::accept_segments(rows, vocab) * sizeof(uint64_t);
+}
+
+attn_status_t attn_mtp_accept(const void* logits, attn_dtype_t logits_dtype, const int32_t* draft_tokens,
+                              int32_t num_seqs, int32_t num_drafts, int32_t vocab, int32_t* target_tokens,
+                              int32_t* num_accepted, void* workspace, size_t workspace_bytes,
+                              hipEvent_t kernel_start, hipEvent_t kernel_stop, hipStream_t stream) {
+  if (!logits || !target_tokens || !num_accepted || !workspace) return ATTN_ERR_INVALID_ARGUMENT;
+  if (num_drafts > 0 && !draft_tokens) return ATTN_ERR_INVALID_ARGUMENT;
+  if (logits_dtype != ATTN_DTYPE_F32 && logits_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARGUMENT;
+  if (num_seqs < 1 || num_drafts < 0 || vocab < 8 || vocab % 8 != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((kernel_start == nullptr) != (kernel_stop == nullptr)) return ATTN_ERR_INVALID_ARGUMENT;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * (num_drafts + 1);
+  if (rows > 65535) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(logits, 16) || !aligned(workspace, 8) || !aligned(target_tokens, 4) || !aligned(num_accepted, 4) ||
+      (draft_tokens && !aligned(draft_tokens, 4)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < attn_mtp_accept_workspace_size(num_seqs, num_drafts, vocab)) return ATTN_ERR_INVALID_ARGUMENT;
+  pa::AcceptParams ap{};
+  ap.logits = logits;
+  ap.drafts = draft_tokens;
+  ap.target_tokens = target_tokens;
+  ap.num_accepted = num_accepted;
+  ap.partial = static_cast<uint64_t*>(workspace);
+  ap.num_seqs = num_seqs;
+  ap.num_drafts = num_drafts;
+  ap.vocab = vocab;
+  ap.segments = pa::accept_segments(rows, vocab);
+  const hipError_t e = pa::launch_mtp_accept(ap, logits_dtype == ATTN_DTYPE_F32, stream, kernel_start, kernel_stop);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
 attn_status_t attn_debug_encode_fp8(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
   if (n < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (n == 0) return ATTN_OK;

@@ -114,6 +114,23 @@ hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool new_f32, h
                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_debug_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
+// Greedy MTP acceptance: K + 1 logits rows per sequence.
+struct AcceptParams {
+  const void* logits;          // [B][K+1][V] bf16 or fp32
+  const int32_t* drafts;       // [B][K]
+  int32_t* target_tokens;      // [B][K+1]
+  int32_t* num_accepted;       // [B]
+  uint64_t* partial;           // [B (K+1)][segments] workspace
+  int32_t num_seqs;
+  int32_t num_drafts;
+  int64_t vocab;               // a multiple of 8
+  int32_t segments;            // workgroups per row
+};
+
+int accept_segments(int64_t rows, int64_t vocab);
+hipError_t launch_mtp_accept(const AcceptParams& p, bool f32, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                             hipEvent_t ev_stop = nullptr);
+
 hipError_t launch_debug_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
 

@@ -80,3 +80,6 @@ def test_null_arguments_rejected():
     assert lib.attn_debug_encode_fp8(None, None, -1, None) == 1
     assert lib.attn_debug_encode_fp8(None, None, 0, None) == 0
     assert lib.attn_debug_encode_fp8(None, None, 3, None) == 1
+    assert lib.attn_mtp_accept(None, 1, None, 1, 4, 64, None, None, None, 0, None, None, None) == 1
+    assert lib.attn_mtp_accept_workspace_size(0, 4, 64) == 0
+    assert lib.attn_mtp_accept_workspace_size(128, 4, 151936) > 0
