@@ -101,8 +101,26 @@ def gather_sequence(k_pages, v_pages, kv_scales, block_table_row, ctx_len: int) 
     return GatheredSequence(kb, vb, ks, vs, pages)
 
 
+def decode_int8(codes) -> np.ndarray:
+    """INT8 KV bytes (two's complement) -> fp64: byte c is c for c < 128,
+    c - 256 otherwise (the quantisation section of the Atlas article lists
+    INT8 beside FP8, with the same per-group scales)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c < 128, c, c - 256).astype(np.float64)
+
+
+def decode_kv(codes, kv_format: str = "e4m3") -> np.ndarray:
+    """KV bytes -> fp64 values before the page scale."""
+    if kv_format == "e4m3":
+        return e4m3.decode(codes)
+    if kv_format == "int8":
+        return decode_int8(codes)
+    raise ValueError(kv_format)
+
+
 def paged_attention(q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, *,
-                    num_kv_heads: int, sm_scale: float | None = None, rows=None) -> np.ndarray:
+                    num_kv_heads: int, sm_scale: float | None = None, rows=None,
+                    kv_format: str = "e4m3") -> np.ndarray:
     """out[r][hq][:] = sum_t softmax_t(z) * V~[t], z_t = scale * <q[r][hq], K~[t]>.
 
     q: [sum Q][Hq][D] (any real dtype; read exactly into fp64).
@@ -125,8 +143,8 @@ def paged_attention(q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_len
         mine = [i for i in range(Q) if want is None or (row0 + i) in want]
         if mine:
             g = gather_sequence(k_pages, v_pages, kv_scales, block_table[b], L)
-            k_deq = [e4m3.decode(g.k_bytes[h]) * g.k_scale[h][:, None] for h in range(num_kv_heads)]
-            v_deq = [e4m3.decode(g.v_bytes[h]) * g.v_scale[h][:, None] for h in range(num_kv_heads)]
+            k_deq = [decode_kv(g.k_bytes[h], kv_format) * g.k_scale[h][:, None] for h in range(num_kv_heads)]
+            v_deq = [decode_kv(g.v_bytes[h], kv_format) * g.v_scale[h][:, None] for h in range(num_kv_heads)]
             idx = np.array(mine)
             lim = np.array([last_visible_key(L, Q, i) for i in mine])  # [n]
             visible = np.arange(L)[None, :] <= lim[:, None]  # [n][L]

@@ -76,6 +76,7 @@ class Workload:
     seed: int = 0
     # Per-sequence logical (unpaged) copies of the quantised K/V, for tests.
     logical: list = field(default_factory=list, repr=False)
+    kv_format: str = "e4m3"  # or "int8": two's-complement bytes, scale = absmax / 127
 
     @property
     def num_seqs(self) -> int:
@@ -126,6 +127,22 @@ def _quantise_pages(x: np.ndarray, valid_slots: np.ndarray):
     return codes, scale
 
 
+def _quantise_pages_int8(x: np.ndarray, valid_slots: np.ndarray):
+    """INT8 variant of _quantise_pages: scale = fp32(absmax) / 127 (1.0 if
+    absmax is 0), byte = round-half-even of fp32(x / scale) clipped to +-127,
+    stored two's complement; poison in unused slots."""
+    n, hkv, s, d = x.shape
+    slot_ok = np.arange(s)[None, :] < valid_slots[:, None]
+    masked = np.where(slot_ok[:, None, :, None], np.abs(x), np.float32(0))
+    absmax = masked.reshape(n, hkv, s * d).max(axis=2).astype(np.float32)
+    scale = (absmax / np.float32(127.0)).astype(np.float32)
+    scale = np.where(absmax > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = (x / scale[:, :, None, None]).astype(np.float32)
+    codes = np.clip(np.rint(y), -127, 127).astype(np.int8).view(np.uint8)
+    codes = np.where(slot_ok[:, None, :, None], codes, np.uint8(POISON_BYTE)).astype(np.uint8)
+    return codes, scale
+
+
 def empty_pages(num_pages: int, num_kv_heads: int, head_dim: int):
     """K and V pools in the ABI layouts, every byte the poison code."""
     if head_dim % 64:
@@ -168,6 +185,7 @@ def build_workload(
     num_kv_splits: int = 0,
     seed: int = 0,
     keep_logical: bool = True,
+    kv_format: str = "e4m3",
 ) -> Workload:
     """Build a workload from drawn lengths, continuing the rng's draw order."""
     S = PAGE_SIZE
@@ -208,10 +226,11 @@ def build_workload(
         valid[first[b] : first[b] + n] = v
 
     k_f = rng.standard_normal((used, num_kv_heads, S, head_dim), dtype=np.float32)
-    k_codes, k_scale = _quantise_pages(k_f, valid)
+    quantise = _quantise_pages_int8 if kv_format == "int8" else _quantise_pages
+    k_codes, k_scale = quantise(k_f, valid)
     del k_f
     v_f = rng.standard_normal((used, num_kv_heads, S, head_dim), dtype=np.float32)
-    v_codes, v_scale = _quantise_pages(v_f, valid)
+    v_codes, v_scale = quantise(v_f, valid)
     del v_f
 
     k_pages, v_pages = empty_pages(num_pages, num_kv_heads, head_dim)
@@ -257,6 +276,7 @@ def build_workload(
         num_kv_splits=num_kv_splits,
         seed=seed,
         logical=logical,
+        kv_format=kv_format,
     )
 
 
@@ -292,7 +312,7 @@ def make_workload(name: str, seed: int | None = None, *, batch: int | None = Non
         raise KeyError(name)
     seed = CONFIGS[name]["seed"] if seed is None else seed
     rng = np.random.default_rng(seed)
-    kw = dict(keep_logical=keep_logical, seed=seed)
+    kw = dict(keep_logical=keep_logical, seed=seed, kv_format=over.get("kv_format", "e4m3"))
 
     if name == "tiny_decode":
         B = batch or 1
@@ -361,10 +381,12 @@ def make_workload(name: str, seed: int | None = None, *, batch: int | None = Non
 
 def custom_workload(q_lens, ctx_lens, *, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=0,
                     q_dtype="bf16", out_dtype="bf16", num_kv_splits=0, max_ctx_len=None,
-                    max_q_len=None, num_pages=None, keep_logical=True, name="custom") -> Workload:
+                    max_q_len=None, num_pages=None, keep_logical=True, name="custom",
+                    kv_format="e4m3") -> Workload:
     """Explicit lengths (edge cases): same recipe, lengths given instead of drawn."""
     rng = np.random.default_rng(seed)
     return build_workload(name, rng, q_lens=q_lens, ctx_lens=ctx_lens, num_q_heads=num_q_heads,
                           num_kv_heads=num_kv_heads, head_dim=head_dim, q_dtype=q_dtype,
                           out_dtype=out_dtype, num_kv_splits=num_kv_splits, max_ctx_len=max_ctx_len,
-                          max_q_len=max_q_len, num_pages=num_pages, keep_logical=keep_logical, seed=seed)
+                          max_q_len=max_q_len, num_pages=num_pages, keep_logical=keep_logical, seed=seed,
+                          kv_format=kv_format)

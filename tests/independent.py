@@ -43,6 +43,12 @@ def e4m3_by_bits(x: int) -> float:
     return struct.unpack("<f", struct.pack("<I", bits))[0]
 
 
+def int8_by_torch(codes) -> np.ndarray:
+    """The library reading of INT8 bytes (torch's int8 view)."""
+    t = torch.as_tensor(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.int8).to(torch.float64).numpy()
+
+
 def e4m3_by_torch(codes) -> np.ndarray:
     t = torch.as_tensor(np.asarray(codes, dtype=np.uint8))
     return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -57,7 +63,10 @@ def brute_force_attention(w) -> np.ndarray:
     ksc = w.kv_scales[0].reshape(-1).tolist()
     vsc = w.kv_scales[1].reshape(-1).tolist()
     q = w.q.double().numpy()
-    dec = [e4m3_by_bits(c) for c in range(256)]
+    if getattr(w, "kv_format", "e4m3") == "int8":
+        dec = [float(c - 256 if c & 0x80 else c) for c in range(256)]  # two's complement
+    else:
+        dec = [e4m3_by_bits(c) for c in range(256)]
     scale = w.sm_scale if w.sm_scale else 1.0 / math.sqrt(D)
     out = np.zeros(q.shape, dtype=np.float64)
     row = 0
@@ -104,8 +113,9 @@ def sdpa_attention(w) -> np.ndarray:
     for b in range(w.num_seqs):
         L, Q = int(w.ctx_lens[b]), int(w.q_lens[b])
         lg = w.logical[b]
-        k = torch.from_numpy(e4m3_by_torch(lg["k_bytes"]) * lg["k_scale"][:, :, None].astype(np.float64))
-        v = torch.from_numpy(e4m3_by_torch(lg["v_bytes"]) * lg["v_scale"][:, :, None].astype(np.float64))
+        dec = int8_by_torch if getattr(w, "kv_format", "e4m3") == "int8" else e4m3_by_torch
+        k = torch.from_numpy(dec(lg["k_bytes"]) * lg["k_scale"][:, :, None].astype(np.float64))
+        v = torch.from_numpy(dec(lg["v_bytes"]) * lg["v_scale"][:, :, None].astype(np.float64))
         qb = q_all[row : row + Q].permute(1, 0, 2).contiguous()  # [Hq][Q][D]
         # bottom-right causal mask: query i sits at position L-Q+i
         qpos = torch.arange(Q)[:, None] + (L - Q)
