@@ -193,7 +193,8 @@ def workload_config(w) -> dict:
         "ctx_min": int(w.ctx_lens.min()),
         "ctx_max": int(w.ctx_lens.max()),
         "ctx_mean": float(w.ctx_lens.mean()),
-        "kv_format": "fp8_e4m3 (OCP), fp32 scale per (page, kv head)",
+        "kv_format": ("int8 (two's complement), fp32 scale per (page, kv head)" if w.kv_format == "int8"
+                      else "fp8_e4m3 (OCP), fp32 scale per (page, kv head)"),
         "q_dtype": w.q_dtype,
         "out_dtype": w.out_dtype,
         "seed": w.seed,
@@ -215,6 +216,11 @@ def attention_kernel_name(info: dict) -> str:
 
 def counter_summary_path(workload: str, kernel: str = "attn_stream_kernel") -> str:
     return os.path.join(PROFILES, f"{kernel}_{workload}_hbm_counters.txt")
+
+
+def profile_name(w) -> str:
+    """Workload name of a counter summary: INT8-KV runs have their own."""
+    return w.name + ("_int8" if getattr(w, "kv_format", "e4m3") == "int8" else "")
 
 
 def committed_traffic(workload: str, kernel: str = "attn_stream_kernel"):
@@ -377,6 +383,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--kv-format", default="e4m3", choices=["e4m3", "int8"],
+                    help="KV byte format of the attention workloads (INT8: two's complement times the page scale)")
     ap.add_argument("--json-out", default=None)
     args = ap.parse_args()
 
@@ -417,13 +425,14 @@ def main():
         and a rotation of KV pool copies of >= 1 GiB."""
 
         def __init__(self, name):
-            w = make_workload(name, keep_logical=False)
+            w = make_workload(name, keep_logical=False, kv_format=args.kv_format)
             self.w = w
             self.counts = algorithmic_counts(w)
             self.plan = Plan(num_seqs=w.num_seqs, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                              head_dim=w.head_dim, num_pages=w.num_pages, max_pages_per_seq=w.max_pages_per_seq,
                              max_q_len=w.max_q_len, max_ctx_len=w.max_ctx_len, q_dtype=w.q_dtype,
-                             out_dtype=w.out_dtype, sm_scale=w.sm_scale, num_kv_splits=w.num_kv_splits)
+                             out_dtype=w.out_dtype, sm_scale=w.sm_scale, num_kv_splits=w.num_kv_splits,
+                             kv_format=w.kv_format)
             self.q = w.q.to(dev)
             self.bt = t(w.block_table)
             self.ctx = t(w.ctx_lens)
@@ -605,7 +614,7 @@ def main():
 
     # the dominant kernel: the attention kernel with the largest share of the step
     dom = max(parts, key=lambda pt: pt.attn_ms)
-    roof = roofline(dom, committed_traffic(dom.w.name, dom.kernel))
+    roof = roofline(dom, committed_traffic(profile_name(dom.w), dom.kernel))
     if len(parts) > 1:
         roof["workload_part"] = dom.w.name
 
@@ -647,7 +656,7 @@ def main():
         "cpu_baseline": None,
     }
     if len(parts) > 1:
-        res["parts"] = [{"workload": pt.w.name, "roofline": roofline(pt, committed_traffic(pt.w.name, pt.kernel))}
+        res["parts"] = [{"workload": pt.w.name, "roofline": roofline(pt, committed_traffic(profile_name(pt.w), pt.kernel))}
                         for pt in parts]
     if args.workload in APPEND_WORKLOADS:
         res["dtype"] = "f32 (IEEE divide) -> fp8 e4m3"

@@ -23,8 +23,8 @@
  * Result (exact arithmetic): for sequence b with L_b keys and Q_b new query
  * tokens, new token i (0-based) and query head hq,
  *     h      = hq / (Hq / Hkv)                       (kv head of the group)
- *     K~[t]  = e4m3(k byte of token t, head h) * kv_scales[0][page(t)][h]
- *     V~[t]  = e4m3(v byte of token t, head h) * kv_scales[1][page(t)][h]
+ *     K~[t]  = dec(k byte of token t, head h) * kv_scales[0][page(t)][h]
+ *     V~[t]  = dec(v byte of token t, head h) * kv_scales[1][page(t)][h]
  *     z_t    = sm_scale * <q[r_b+i][hq][:], K~[t]>   for t <= L_b - Q_b + i
  *     out[r_b+i][hq][:] = sum_t softmax(z)_t * V~[t]
  * where r_b = Q_0 + ... + Q_{b-1} and page(t) = block_table[b][t / 16].
@@ -45,8 +45,8 @@
  *   q_lens      int32 [B]   Q_b
  *   out         [sum Q_b][Hq][D]  ATTN_DTYPE_BF16 (round to nearest even)
  *               or ATTN_DTYPE_F32
- * E4M3 is the OCP 8-bit floating point E4M3 format (bias 7, max 448, NaN
- * only at 0x7F/0xFF).
+ * dec() is the OCP 8-bit floating point E4M3 format (bias 7, max 448, NaN
+ * only at 0x7F/0xFF) by default, or a signed INT8 (desc.kv_format).
  *
  * Device-data preconditions (not checked on the hot path; breaking one is
  * undefined and may fault):
@@ -88,6 +88,14 @@ typedef enum {
 
 typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype_t;
 
+/* Format of the K/V bytes in the pages.  The quantisation section of the
+ * Atlas article lists INT4/INT8/FP8 with per-group scales; with ATTN_KV_INT8
+ * a byte is a two's-complement integer in [-128, 127] and its value is that
+ * integer times the page's scale (the same scales, layouts and rules as
+ * E4M3 otherwise).  INT8 plans take BF16 q and out; attn_kv_append writes
+ * E4M3 only (ATTN_ERR_UNSUPPORTED for an INT8 plan). */
+typedef enum { ATTN_KV_E4M3 = 0, ATTN_KV_INT8 = 1 } attn_kv_format_t;
+
 /* Static shape of the work a plan serves (the "adaptive tiling" of the
  * attention section: tile and split sizes are chosen from it once). */
 typedef struct {
@@ -108,7 +116,8 @@ typedef struct {
                                 cut into segments * n equal contiguous
                                 partitions (so each of equal-length segments
                                 gets exactly n), merged by log-sum-exp */
-  int32_t reserved[4];       /* must be zero */
+  int32_t kv_format;         /* ATTN_KV_E4M3 (0) or ATTN_KV_INT8 (1) */
+  int32_t reserved[3];       /* must be zero */
 } attn_plan_desc_t;
 
 /* What the plan chose (for tests and measurement).  A segment is one

@@ -60,7 +60,8 @@ class PlanDesc(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("num_kv_splits", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("kv_format", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -170,7 +171,7 @@ class Plan:
 
     def __init__(self, *, num_seqs, num_q_heads, num_kv_heads, head_dim, num_pages, max_pages_per_seq,
                  max_q_len, max_ctx_len, q_dtype="bf16", out_dtype="bf16", sm_scale=0.0, num_kv_splits=0,
-                 page_size=16, reserved=(0, 0, 0, 0)):
+                 page_size=16, kv_format="e4m3", reserved=(0, 0, 0)):
         lib = load_library()
         d = PlanDesc()
         d.num_seqs = num_seqs
@@ -186,6 +187,7 @@ class Plan:
         d.out_dtype = _dtype_code(out_dtype)
         d.sm_scale = float(sm_scale)
         d.num_kv_splits = num_kv_splits
+        d.kv_format = {"e4m3": 0, "int8": 1}.get(kv_format, kv_format) if isinstance(kv_format, str) else kv_format
         for i, r in enumerate(reserved):
             d.reserved[i] = r
         self.desc = d

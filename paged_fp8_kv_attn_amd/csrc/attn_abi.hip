@@ -85,6 +85,9 @@ attn_status_t validate_desc(const attn_plan_desc_t& d) {
   if (d.out_dtype != ATTN_DTYPE_F32 && d.out_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARGUMENT;
   if (!(d.sm_scale >= 0.f) || !std::isfinite(d.sm_scale)) return ATTN_ERR_INVALID_ARGUMENT;
   if (d.num_kv_splits < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.kv_format != ATTN_KV_E4M3 && d.kv_format != ATTN_KV_INT8) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.kv_format == ATTN_KV_INT8 && (d.q_dtype != ATTN_DTYPE_BF16 || d.out_dtype != ATTN_DTYPE_BF16))
+    return ATTN_ERR_UNSUPPORTED;
   if (d.page_size != pa::kPageSize) return ATTN_ERR_UNSUPPORTED;
   if (d.head_dim != 64 && d.head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(d.max_pages_per_seq) * d.page_size < d.max_ctx_len) return ATTN_ERR_INVALID_ARGUMENT;
@@ -127,6 +130,7 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   v.head_dim = d.head_dim;
   v.q_f32 = d.q_dtype == ATTN_DTYPE_F32;
   v.out_f32 = d.out_dtype == ATTN_DTYPE_F32;
+  v.kv_int8 = d.kv_format == ATTN_KV_INT8;
   if (cols <= 4) {  // four pages per score tile
     v.col_tiles = 1;
     v.packed = true;
@@ -391,6 +395,7 @@ attn_status_t attn_kv_append(attn_plan_t plan, const void* k_new, const void* v_
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
       !aligned(kv_scales, 4) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) || !aligned(q_lens, 4))
     return ATTN_ERR_INVALID_ARGUMENT;
+  if (plan->desc.kv_format != ATTN_KV_E4M3) return ATTN_ERR_UNSUPPORTED;
   const attn_status_t dst = check_device(plan);
   if (dst != ATTN_OK) return dst;
   const attn_plan_desc_t& d = plan->desc;

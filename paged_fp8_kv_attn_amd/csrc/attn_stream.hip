@@ -292,7 +292,7 @@ struct PieceDesc {
   int slot;            // partial slot when not whole
 };
 
-template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int NBUF>
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int NBUF, bool KI8>
 __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc& pc, int lane, int wave) {
   using GD = Geo<D>;
   constexpr int NW = kWavesPerGroup;
@@ -453,7 +453,7 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
 #pragma unroll
       for (int s = 0; s < GD::NSLAB; ++s) {
         const u32x4 w = kc[pg][(2 * s) / 4];
-        const bf16x8 kb = fp8x8_to_bf16x8(w[(2 * s) % 4], w[(2 * s) % 4 + 1]);
+        const bf16x8 kb = kv8x8_to_bf16x8<KI8>(w[(2 * s) % 4], w[(2 * s) % 4 + 1]);
 #pragma unroll
         for (int t = 0; t < NCT; ++t) {
 #pragma unroll
@@ -548,7 +548,7 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
     for (int cblk = 0; cblk < GD::NVB; ++cblk) {
       const uint32_t w0 = vc[0][cblk / 4][cblk % 4] & vmask0;
       const uint32_t w1 = vc[1][cblk / 4][cblk % 4] & vmask1;
-      const bf16x8 va = fp8x8_to_bf16x8(w0, w1);
+      const bf16x8 va = kv8x8_to_bf16x8<KI8>(w0, w1);
 #pragma unroll
       for (int t = 0; t < NCT; ++t) {
         o[t][cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi[t], o[t][cblk], 0, 0, 0);
@@ -693,7 +693,7 @@ __device__ __forceinline__ float dpp_ror8(float x) {
   return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x128 /*row_ror:8*/, 0xf, 0xf, false));
 }
 
-template <int D, bool QF32, bool OUTF32, int NRING>
+template <int D, bool QF32, bool OUTF32, int NRING, bool KI8>
 __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const PieceDesc& pc, int lane) {
   using GD = Geo<D>;
   constexpr int NP = QF32 ? 3 : 1;
@@ -839,7 +839,7 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
 #pragma unroll
       for (int s = 0; s < GD::NSLAB; ++s) {
         const u32x4 w = kc[pg][(2 * s) / 4];
-        const bf16x8 kb = fp8x8_to_bf16x8(w[(2 * s) % 4], w[(2 * s) % 4 + 1]);
+        const bf16x8 kb = kv8x8_to_bf16x8<KI8>(w[(2 * s) % 4], w[(2 * s) % 4 + 1]);
 #pragma unroll
         for (int part = 0; part < NP; ++part)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[part][s], acc, 0, 0, 0);
@@ -904,7 +904,7 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
       for (int cblk = 0; cblk < GD::NVB; ++cblk) {
         const uint32_t w0 = vc[2 * ch][cblk / 4][cblk % 4] & vm0;
         const uint32_t w1 = vc[2 * ch + 1][cblk / 4][cblk % 4] & vm1;
-        const bf16x8 va = fp8x8_to_bf16x8(w0, w1);
+        const bf16x8 va = kv8x8_to_bf16x8<KI8>(w0, w1);
         o[cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bhi, o[cblk], 0, 0, 0);
         o[cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, blo, o[cblk], 0, 0, 0);
       }
@@ -1090,7 +1090,7 @@ __device__ __forceinline__ void load_q_operand(const StreamParams& p, size_t qof
   }
 }
 
-template <int D, int NW, int NT, bool QF32, bool OUTF32, int R>
+template <int D, int NW, int NT, bool QF32, bool OUTF32, int R, bool KI8>
 __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const PieceDesc& pc, int lane, int wave) {
   using GD = Geo<D>;
   using TG = TileGeo<D, NW>;
@@ -1214,8 +1214,8 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
       const int jj = r * NW + wave;
       if (jj < 2 * GD::NKV) {
         const int s0 = ldpg[r] * GD::NSLAB + 2 * (jj % GD::NKV);
-        dst[s0][lane] = fp8x8_to_bf16x8(w[0], w[1]);
-        dst[s0 + 1][lane] = fp8x8_to_bf16x8(w[2], w[3]);
+        dst[s0][lane] = kv8x8_to_bf16x8<KI8>(w[0], w[1]);
+        dst[s0 + 1][lane] = kv8x8_to_bf16x8<KI8>(w[2], w[3]);
       } else {
         // V bytes of keys >= L may be anything (NaN codes included): zero them
         const int key0 = c * kChunk + 16 * ldpg[r] + 4 * lq;
@@ -1228,7 +1228,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
         const int i = (jj - 2 * GD::NKV) % GD::NVV;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          reinterpret_cast<bf16x4*>(&dst[TG::KSL + 4 * i + e][lane])[ldpg[r]] = fp8x4_to_bf16x4(w[e] & vm);
+          reinterpret_cast<bf16x4*>(&dst[TG::KSL + 4 * i + e][lane])[ldpg[r]] = kv8x4_to_bf16x4<KI8>(w[e] & vm);
       }
     }
 #pragma unroll
@@ -1453,7 +1453,7 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
 // 4 waves take the chunks of a piece in turn (the workgroup is the unit).
 // Two waves per SIMD (256 registers each), one for the packed layout with
 // two groups in flight.
-template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int PR>
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int PR, bool KI8>
 __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
                              (NCT == 0 ? (PR == 1 ? 2 : 1) : 2)) void attn_stream_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
@@ -1469,9 +1469,9 @@ __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
   walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
     if constexpr (NCT == 0) {
       // at most 4 query columns: four pages per score tile
-      run_piece_packed<D, QF32, OUTF32, PR>(p, pc, lane);
+      run_piece_packed<D, QF32, OUTF32, PR, KI8>(p, pc, lane);
     } else {
-      run_piece<D, NCT, DUPLO, QF32, OUTF32, 2>(p, pc, lane, wave);
+      run_piece<D, NCT, DUPLO, QF32, OUTF32, 2, KI8>(p, pc, lane, wave);
     }
   });
 }
@@ -1496,7 +1496,7 @@ struct TileCfg {
   static constexpr int WAVES_PER_SIMD = 2;
 };
 
-template <int D, int NW, int NT, bool QF32, bool OUTF32>
+template <int D, int NW, int NT, bool QF32, bool OUTF32, bool KI8>
 __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void attn_tile_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1509,7 +1509,7 @@ __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void at
   const int W = work_units(p, T);
   if (w >= W) return;
   walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
-    run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R>(p, pc, lane, wave);
+    run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KI8>(p, pc, lane, wave);
   });
 }
 
@@ -1635,18 +1635,22 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(StreamParams
 
 template <int D, int NCT, bool DUPLO, int PR = 1>
 static const void* kernel_d(const Variant& v) {
-  if (v.q_f32 && v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, true, PR>);
-  if (v.q_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, false, PR>);
-  if (v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, true, PR>);
-  return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR>);
+  // INT8 KV: bf16 Q and output only (the plan rejects the rest)
+  if (v.kv_int8) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR, true>);
+  if (v.q_f32 && v.out_f32)
+    return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, true, PR, false>);
+  if (v.q_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, false, PR, false>);
+  if (v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, true, PR, false>);
+  return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR, false>);
 }
 
 template <int D, int NW, int NT>
 static const void* tile_d(const Variant& v) {
-  if (v.q_f32 && v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, true>);
-  if (v.q_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, false>);
-  if (v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, true>);
-  return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false>);
+  if (v.kv_int8) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, true>);
+  if (v.q_f32 && v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, true, false>);
+  if (v.q_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, false, false>);
+  if (v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, true, false>);
+  return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, false>);
 }
 
 template <int D>

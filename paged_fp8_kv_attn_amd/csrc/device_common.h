@@ -78,6 +78,44 @@ __device__ __forceinline__ f32x4 fp8x4_to_f32x4(uint32_t w) {
   return f32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Four INT8 bytes (two's complement) -> four bf16, exactly: byte b becomes
+// the fp32 value 2^23 + (b XOR 0x80) (its bits 0x4B0000uu), minus 2^23 + 128,
+// and every integer in [-128, 127] is a bf16 value.
+__device__ __forceinline__ bf16x4 i8x4_to_bf16x4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  float f[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    f[e] = __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, u, 0x070C0C00u | (uint32_t)e)) - 8388736.0f;
+  const bf16x2 a = __builtin_convertvector(f32x2{f[0], f[1]}, bf16x2);
+  const bf16x2 b = __builtin_convertvector(f32x2{f[2], f[3]}, bf16x2);
+  return bf16x4{a[0], a[1], b[0], b[1]};
+}
+
+// Eight KV bytes -> eight bf16 in order: OCP E4M3 codes, or INT8 with KI8.
+template <bool KI8>
+__device__ __forceinline__ bf16x8 kv8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  if constexpr (KI8) {
+    const bf16x4 a = i8x4_to_bf16x4(w0);
+    const bf16x4 b = i8x4_to_bf16x4(w1);
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  } else {
+    return fp8x8_to_bf16x8(w0, w1);
+  }
+}
+
+// Four KV bytes -> four bf16 in order.
+template <bool KI8>
+__device__ __forceinline__ bf16x4 kv8x4_to_bf16x4(uint32_t w) {
+  if constexpr (KI8) {
+    return i8x4_to_bf16x4(w);
+  } else {
+    const bf16x2 a = fp8x2_to_bf16x2<false>(w);
+    const bf16x2 b = fp8x2_to_bf16x2<true>(w);
+    return bf16x4{a[0], a[1], b[0], b[1]};
+  }
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

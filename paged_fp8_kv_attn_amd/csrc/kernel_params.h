@@ -47,6 +47,7 @@ struct Variant {
   bool dup_lo;      // low halves of P in spare columns (col_tiles == 1, <= 8 columns)
   bool q_f32;
   bool out_f32;
+  bool kv_int8;     // KV bytes are INT8 (two's complement) instead of OCP E4M3
 };
 
 constexpr int kWavesPerGroup = 4;
