@@ -19,6 +19,10 @@ Readings where the pages are silent (each listed in the design notes):
   * Encoding: the finite E4M3 code nearest to fp32(value / scale), ties to
     the code with an even mantissa, magnitudes above 448 saturated to 448,
     the sign kept (a negative value that rounds to zero gives -0, 0x80).
+  * INT8 pools (the quantisation section lists INT8 beside FP8): the same
+    steps with scale = fp32(absmax) / 127 and the integer nearest to
+    fp32(value / scale), ties to even, clipped to +-127, stored two's
+    complement.
   * Slots at or past the sequence's new length keep whatever they held;
     pages the sequence does not touch are not written.
   * New token i of sequence b (0 <= i < Q_b) is key L_b - Q_b + i; its K/V
@@ -63,6 +67,25 @@ def encode(y) -> np.ndarray:
     return (code | sign).astype(np.uint8)
 
 
+INT8_MAX = 127.0
+
+
+def encode_int8(y) -> np.ndarray:
+    """fp32 values -> INT8 bytes (two's complement): round half to even,
+    clipped to +-127."""
+    y = np.asarray(y, dtype=np.float32)
+    q = np.clip(np.rint(y.astype(np.float64)), -INT8_MAX, INT8_MAX).astype(np.int64)
+    return (q & 0xFF).astype(np.uint8)
+
+
+def page_scale_int8(absmax) -> np.float32:
+    """fp32(absmax) / 127 in fp32; 1 for an all-zero page."""
+    a = np.float32(absmax)
+    if a == 0:
+        return np.float32(1.0)
+    return np.float32(a / np.float32(INT8_MAX))
+
+
 def page_scale(absmax) -> np.float32:
     """fp32(absmax) / 448 in fp32; 1 for an all-zero page."""
     a = np.float32(absmax)
@@ -86,11 +109,22 @@ def _set_v_bytes(v_pages, page, h, slot, row):
     v_pages[page, h, slot // 4, :, :, :, slot % 4] = a_i_e.transpose(1, 0, 2)
 
 
-def kv_append(k_new, v_new, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, *, page_size: int = 16):
+def kv_append(k_new, v_new, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, *, page_size: int = 16,
+              kv_format: str = "e4m3"):
     """Quantise the new tokens' K and V into copies of the pools.
 
     k_new, v_new: [sum Q][Hkv][D] (any real dtype; read exactly as fp32).
+    kv_format "int8": the same steps with scale = fp32(absmax)/127 and
+    round-half-even integer codes clipped to +-127 (two's complement).
     Returns (k_pages, v_pages, kv_scales) after the append."""
+    from .attention import decode_kv
+
+    if kv_format == "int8":
+        scale_of, encode_fn = page_scale_int8, encode_int8
+    elif kv_format == "e4m3":
+        scale_of, encode_fn = page_scale, encode
+    else:
+        raise ValueError(kv_format)
     if hasattr(k_new, "detach"):
         k_new = k_new.detach().to("cpu").float().numpy()
     if hasattr(v_new, "detach"):
@@ -121,12 +155,13 @@ def kv_append(k_new, v_new, k_pages, v_pages, kv_scales, block_table, ctx_lens, 
                     vals = np.empty((valid, new_rows.shape[2]), dtype=np.float32)
                     if n_old:
                         old = read_bytes(pool, np.full(n_old, page), h, slots[:n_old])
-                        vals[:n_old] = (e4m3.decode(old) * np.float64(kv_scales[which][page, h])).astype(np.float32)
+                        vals[:n_old] = (decode_kv(old, kv_format) * np.float64(kv_scales[which][page, h])).astype(
+                            np.float32)
                     for s in range(n_old, valid):
                         vals[s] = new_rows[row0 + (pi * S + s - first_new), h]
-                    scale = page_scale(np.max(np.abs(vals)))
+                    scale = scale_of(np.max(np.abs(vals)))
                     kv_scales[which][page, h] = scale
-                    codes = encode((vals / scale).astype(np.float32))
+                    codes = encode_fn((vals / scale).astype(np.float32))
                     for s in range(valid):
                         write_bytes(pool, page, h, s, codes[s])
         row0 += Q

@@ -20,7 +20,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from .workloads import PAGE_SIZE, POISON_BYTE, _quantise_pages, empty_pages, k_to_layout, v_to_layout
+from .workloads import (PAGE_SIZE, POISON_BYTE, _quantise_pages, _quantise_pages_int8, empty_pages, k_to_layout,
+                        v_to_layout)
 
 
 @dataclass
@@ -38,6 +39,7 @@ class AppendCase:
     k_new: torch.Tensor  # [sum Q][Hkv][D] new_dtype (CPU)
     v_new: torch.Tensor
     seed: int = 0
+    kv_format: str = "e4m3"  # or "int8" (cached part quantised to two's-complement bytes, absmax / 127)
 
     @property
     def num_seqs(self) -> int:
@@ -74,7 +76,8 @@ def _round(x: np.ndarray, dtype: str) -> torch.Tensor:
 
 
 def append_case(q_lens, ctx_lens, *, num_kv_heads=8, head_dim=128, new_dtype="bf16", seed=0,
-                new_sigmas=(0.5, 1.0, 2.0), num_pages=None, max_pages_per_seq=None, name="append") -> AppendCase:
+                new_sigmas=(0.5, 1.0, 2.0), num_pages=None, max_pages_per_seq=None, name="append",
+                kv_format="e4m3") -> AppendCase:
     S = PAGE_SIZE
     q_lens = np.asarray(q_lens, dtype=np.int32)
     ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
@@ -105,7 +108,8 @@ def append_case(q_lens, ctx_lens, *, num_kv_heads=8, head_dim=128, new_dtype="bf
     for which in range(2):
         x = rng.standard_normal((used, num_kv_heads, S, head_dim), dtype=np.float32)
         if idx.size:
-            codes, scale = _quantise_pages(x[idx], cached_slots[idx])
+            quantise = _quantise_pages_int8 if kv_format == "int8" else _quantise_pages
+            codes, scale = quantise(x[idx], cached_slots[idx])
             pool = k_pages if which == 0 else v_pages
             pool[phys[idx]] = k_to_layout(codes) if which == 0 else v_to_layout(codes)
             kv_scales[which, phys[idx]] = scale
@@ -118,7 +122,8 @@ def append_case(q_lens, ctx_lens, *, num_kv_heads=8, head_dim=128, new_dtype="bf
     v_new = rng.standard_normal((total_q, num_kv_heads, head_dim), dtype=np.float32) * rows_sigma
     return AppendCase(name=name, num_kv_heads=num_kv_heads, head_dim=head_dim, new_dtype=new_dtype, q_lens=q_lens,
                       ctx_lens=ctx_lens, block_table=block_table, k_pages=k_pages, v_pages=v_pages,
-                      kv_scales=kv_scales, k_new=_round(k_new, new_dtype), v_new=_round(v_new, new_dtype), seed=seed)
+                      kv_scales=kv_scales, k_new=_round(k_new, new_dtype), v_new=_round(v_new, new_dtype), seed=seed,
+                      kv_format=kv_format)
 
 
 # Append steps of the measured serving shapes: the decode step of the

@@ -146,9 +146,23 @@ def _f32(x: float) -> float:
     return struct.unpack("<f", struct.pack("<f", x))[0]
 
 
-def brute_force_append(c):
+def int8_encode_brute(y: float) -> int:
+    """The integer nearest to y (ties to the even one) clipped to +-127, as a
+    two's-complement byte."""
+    f = math.floor(y)
+    d = y - f
+    q = f + 1 if d > 0.5 or (d == 0.5 and f % 2 == 1) else f
+    q = max(-127, min(127, int(q)))
+    return q & 0xFF
+
+
+def brute_force_append(c, kv_format: str = "e4m3"):
     """Pure-Python loops over flat byte offsets: quantise an AppendCase's new
     rows into copies of its pools (tiny cases only)."""
+    int8 = kv_format == "int8"
+    qmax = 127.0 if int8 else 448.0
+    dec_tab = [float(b - 256 if b & 0x80 else b) for b in range(256)] if int8 else [e4m3_by_bits(b) for b in range(256)]
+    enc = int8_encode_brute if int8 else e4m3_encode_brute
     S, D, Hkv = 16, c.head_dim, c.num_kv_heads
     kflat = c.k_pages.reshape(-1).copy()
     vflat = c.v_pages.reshape(-1).copy()
@@ -179,13 +193,13 @@ def brute_force_append(c):
                             break
                         for d in range(D):
                             if t < L - Q:
-                                vals[(s, d)] = _f32(e4m3_by_bits(int(flat[off(p, h, s, d)])) * old_scale)
+                                vals[(s, d)] = _f32(dec_tab[int(flat[off(p, h, s, d)])] * old_scale)
                             else:
                                 vals[(s, d)] = float(new[row + t - (L - Q), h, d])
                     amax = max(abs(x) for x in vals.values())
-                    sc = 1.0 if amax == 0 else _f32(amax / 448.0)
+                    sc = 1.0 if amax == 0 else _f32(amax / qmax)
                     scales[which][p, h] = sc
                     for (s, d), x in vals.items():
-                        flat[off(p, h, s, d)] = e4m3_encode_brute(_f32(x / sc))
+                        flat[off(p, h, s, d)] = enc(_f32(x / sc))
         row += Q
     return kflat.reshape(c.k_pages.shape), vflat.reshape(c.v_pages.shape), scales

@@ -198,3 +198,46 @@ def test_append_zero_rows_pin():
     p = c.block_table[0, 0]
     assert s[0, p, 0] == 1.0 and s[1, p, 0] == 1.0
     assert np.all((k[p] & 0x7F) == 0) and np.all((v[p] & 0x7F) == 0)
+
+
+@pytest.mark.parametrize("idx", range(len(TINY)))
+def test_append_int8_brute_force(idx):
+    ql, cl, hkv, d, dt, sig = TINY[idx]
+    c = sa.append_case(ql, cl, num_kv_heads=hkv, head_dim=d, new_dtype=dt, seed=80 + idx, new_sigmas=sig,
+                       kv_format="int8")
+    k, v, s = ka.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.kv_scales, c.block_table, c.ctx_lens,
+                           c.q_lens, kv_format="int8")
+    bk, bv, bs = brute_force_append(c, kv_format="int8")
+    assert np.array_equal(k, bk) and np.array_equal(v, bv)
+    assert np.array_equal(s.view(np.uint32), bs.view(np.uint32))
+
+
+def test_int8_encoder_ties_and_clip():
+    y = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, 127.4, 130.0, -200.0, 0.49999997, -0.0], dtype=np.float32)
+    got = ka.encode_int8(y).view(np.int8).tolist()
+    assert got == [0, 2, 2, 0, -2, -2, 126, 127, 127, -127, 0, 0]
+
+
+def test_int8_fresh_pages_match_generator_quantiser():
+    from synth.workloads import _quantise_pages_int8
+
+    c = sa.append_case([37, 16], [37, 16], num_kv_heads=2, head_dim=128, new_dtype="f32", seed=3, kv_format="int8")
+    k, v, s = ka.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.kv_scales, c.block_table, c.ctx_lens,
+                           c.q_lens, kv_format="int8")
+    S = 16
+    row = 0
+    for b in range(c.num_seqs):
+        L = int(c.ctx_lens[b])
+        n = (L + S - 1) // S
+        for which, new, pool in ((0, c.k_new, k), (1, c.v_new, v)):
+            x = np.zeros((n, c.num_kv_heads, S, c.head_dim), dtype=np.float32)
+            xs = new[row:row + L].numpy()
+            for t in range(L):
+                x[t // S, :, t % S] = xs[t]
+            valid = np.minimum(S, L - np.arange(n) * S)
+            codes, scale = _quantise_pages_int8(x, valid)
+            phys = c.block_table[b, :n]
+            want = k_to_layout(codes) if which == 0 else v_to_layout(codes)
+            assert np.array_equal(pool[phys], want)
+            assert np.array_equal(s[which, phys], scale)
+        row += L
