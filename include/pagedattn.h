@@ -92,8 +92,9 @@ typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype_t;
  * Atlas article lists INT4/INT8/FP8 with per-group scales; with ATTN_KV_INT8
  * a byte is a two's-complement integer in [-128, 127] and its value is that
  * integer times the page's scale (the same scales, layouts and rules as
- * E4M3 otherwise).  INT8 plans take BF16 q and out; attn_kv_append writes
- * E4M3 only (ATTN_ERR_UNSUPPORTED for an INT8 plan). */
+ * E4M3 otherwise).  INT8 plans take BF16 q and out; attn_kv_append on an
+ * INT8 plan uses 127 in place of 448 and the integer nearest to
+ * value / scale (ties to even, clipped to +-127). */
 typedef enum { ATTN_KV_E4M3 = 0, ATTN_KV_INT8 = 1 } attn_kv_format_t;
 
 /* Static shape of the work a plan serves (the "adaptive tiling" of the

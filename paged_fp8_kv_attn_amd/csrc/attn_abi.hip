@@ -395,7 +395,6 @@ attn_status_t attn_kv_append(attn_plan_t plan, const void* k_new, const void* v_
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
       !aligned(kv_scales, 4) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) || !aligned(q_lens, 4))
     return ATTN_ERR_INVALID_ARGUMENT;
-  if (plan->desc.kv_format != ATTN_KV_E4M3) return ATTN_ERR_UNSUPPORTED;
   const attn_status_t dst = check_device(plan);
   if (dst != ATTN_OK) return dst;
   const attn_plan_desc_t& d = plan->desc;
@@ -414,8 +413,8 @@ attn_status_t attn_kv_append(attn_plan_t plan, const void* k_new, const void* v_
   // Q new keys starting anywhere in a page span at most ceil(Q/16) + 1 pages
   ap.max_touch = std::min<int>(ceil_div(d.max_q_len, pa::kPageSize) + 1, d.max_pages_per_seq);
   ap.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
-  const hipError_t e = pa::launch_kv_append(ap, d.head_dim, new_dtype == ATTN_DTYPE_F32, stream, plan->ev_start,
-                                            plan->ev_stop);
+  const hipError_t e = pa::launch_kv_append(ap, d.head_dim, new_dtype == ATTN_DTYPE_F32,
+                                            d.kv_format == ATTN_KV_INT8, stream, plan->ev_start, plan->ev_stop);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

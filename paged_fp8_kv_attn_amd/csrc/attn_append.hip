@@ -1,6 +1,7 @@
 // Paged FP8 KV append for gfx950: the new tokens' K and V rows of each
 // sequence are quantised into its pages through the block table, with one
-// fp32 scale per (page, kv head).
+// fp32 scale per (page, kv head).  INT8 pools (KI8) take the same steps
+// with 127 in place of 448 and round-half-even integer codes.
 //
 // Follows the memory section of the Atlas engine article (ainews.cool,
 // "技术深度解析": fixed-size KV blocks from a preallocated pool), its
@@ -80,7 +81,28 @@ __device__ __forceinline__ void load_row(const void* base, int64_t off, float* v
   }
 }
 
-template <int D, bool F32IN>
+// Four INT8 bytes (two's complement) -> four fp32 values, exactly.
+__device__ __forceinline__ f32x4 i8x4_to_f32x4(uint32_t w) {
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = (float)(int8_t)(uint8_t)(w >> (8 * e));
+  return r;
+}
+
+// Four fp32 -> four INT8 bytes: nearest integer, ties to even, clipped to
+// +-127, two's complement (a in byte 0).
+__device__ __forceinline__ uint32_t f32x4_to_i8x4(float a, float b, float c, float d) {
+  const float x[4] = {a, b, c, d};
+  uint32_t w = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(x[e]), -127.f), 127.f);
+    w |= ((uint32_t)(int32_t)q & 0xffu) << (8 * e);
+  }
+  return w;
+}
+
+template <int D, bool F32IN, bool KI8>
 __global__ __launch_bounds__(64 * kAppendWaves) void kv_append_kernel(AppendParams p) {
   constexpr int U = D / 64;     // 16-byte units per lane
   constexpr int NVB = D / 16;   // V: values of d per 16-row block
@@ -186,7 +208,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void kv_append_kernel(AppendPara
     oldw[u] = need_old ? *reinterpret_cast<const u32x4*>(chunk + 16 * j) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f32x4 f = fp8x4_to_f32x4(oldw[u][q]);
+      const f32x4 f = KI8 ? i8x4_to_f32x4(oldw[u][q]) : fp8x4_to_f32x4(oldw[u][q]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int k = 4 * q + e;
@@ -197,7 +219,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void kv_append_kernel(AppendPara
     }
   }
   amax = wave_max(amax);
-  const float scale = (amax == 0.f) ? 1.f : amax / 448.f;
+  const float scale = (amax == 0.f) ? 1.f : amax / (KI8 ? 127.f : 448.f);
   const bool changed = n_old == 0 || __float_as_uint(scale) != __float_as_uint(old_scale);
 
 #pragma unroll
@@ -214,7 +236,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void kv_append_kernel(AppendPara
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = val[u][4 * q + e] / scale;
-      const uint32_t enc = f32x4_to_fp8x4(y[0], y[1], y[2], y[3]);
+      const uint32_t enc = KI8 ? f32x4_to_i8x4(y[0], y[1], y[2], y[3]) : f32x4_to_fp8x4(y[0], y[1], y[2], y[3]);
       // bytes of slots at or past the new length keep their old value
       uint32_t keep = 0u;
 #pragma unroll
@@ -239,19 +261,22 @@ __global__ __launch_bounds__(256) void debug_encode_kernel(const float* in, uint
 
 }  // namespace
 
-hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool new_f32, hipStream_t stream,
+template <int D>
+static const void* append_kernel(bool new_f32, bool kv_int8) {
+  if (kv_int8)
+    return new_f32 ? reinterpret_cast<const void*>(&kv_append_kernel<D, true, true>)
+                   : reinterpret_cast<const void*>(&kv_append_kernel<D, false, true>);
+  return new_f32 ? reinterpret_cast<const void*>(&kv_append_kernel<D, true, false>)
+                 : reinterpret_cast<const void*>(&kv_append_kernel<D, false, false>);
+}
+
+hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool new_f32, bool kv_int8, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int64_t jobs = (int64_t)p.max_touch * 2 * p.num_kv_heads;
   const int64_t gx = (jobs + kAppendWaves - 1) / kAppendWaves;
   if (gx <= 0 || p.num_seqs <= 0) return hipSuccess;
   if (gx > 0x7fffffff || p.num_seqs > 65535) return hipErrorInvalidValue;
-  const void* fn;
-  if (head_dim == 128)
-    fn = new_f32 ? reinterpret_cast<const void*>(&kv_append_kernel<128, true>)
-                 : reinterpret_cast<const void*>(&kv_append_kernel<128, false>);
-  else
-    fn = new_f32 ? reinterpret_cast<const void*>(&kv_append_kernel<64, true>)
-                 : reinterpret_cast<const void*>(&kv_append_kernel<64, false>);
+  const void* fn = head_dim == 128 ? append_kernel<128>(new_f32, kv_int8) : append_kernel<64>(new_f32, kv_int8);
   AppendParams copy = p;
   void* args[] = {&copy};
   return hipExtLaunchKernel(fn, dim3((unsigned)gx, (unsigned)p.num_seqs), dim3(64 * kAppendWaves), args, 0, stream,

@@ -111,7 +111,7 @@ struct AppendParams {
   int64_t v_scale_offset;      // P * Hkv
 };
 
-hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool new_f32, hipStream_t stream,
+hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool new_f32, bool kv_int8, hipStream_t stream,
                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_debug_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 

@@ -44,11 +44,12 @@ def test_encode_bit_exact():
 def _plan_for(c):
     return Plan(num_seqs=c.num_seqs, num_q_heads=c.num_kv_heads, num_kv_heads=c.num_kv_heads, head_dim=c.head_dim,
                 num_pages=c.num_pages, max_pages_per_seq=c.max_pages_per_seq, max_q_len=c.max_q_len,
-                max_ctx_len=c.max_ctx_len)
+                max_ctx_len=c.max_ctx_len, kv_format=c.kv_format)
 
 
 def _append_parity(c):
     log(f"append: {c.name} seed={c.seed} B={c.num_seqs} Hkv={c.num_kv_heads} D={c.head_dim} dtype={c.new_dtype} "
+        f"kv={c.kv_format} "
         f"q=[{c.q_lens.min()},{c.q_lens.max()}] ctx=[{c.ctx_lens.min()},{c.ctx_lens.max()}]")
     dev = "cuda"
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
@@ -59,7 +60,7 @@ def _append_parity(c):
     torch.cuda.synchronize()
     plan.close()
     ok, ov, os_ = ka.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.kv_scales, c.block_table, c.ctx_lens,
-                               c.q_lens)
+                               c.q_lens, kv_format=c.kv_format)
     gk, gv, gs = k.cpu().numpy(), v.cpu().numpy(), s.cpu().numpy()
     nk = int((gk != ok).sum())
     nv = int((gv != ov).sum())
@@ -97,3 +98,10 @@ def test_append_prefill_reduced():
 
 def test_append_prefill_full():
     _append_parity(sa.make_append_case("append_prefill"))
+
+
+@pytest.mark.parametrize("idx", range(len(CASES)))
+def test_append_cases_int8(idx):
+    ql, cl, hkv, d, dt, sig = CASES[idx]
+    _append_parity(sa.append_case(ql, cl, num_kv_heads=hkv, head_dim=d, new_dtype=dt, seed=90 + idx,
+                                  new_sigmas=sig, name=f"append_int8_edge{idx}", kv_format="int8"))
