@@ -390,7 +390,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention path runs whole on a single MI355X "
-              "and this build has no multi-GPU mode (use --gpus 1).", file=sys.stderr)
+              "and this library has no multi-GPU mode (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch

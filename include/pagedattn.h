@@ -81,7 +81,7 @@ typedef struct attn_plan_s* attn_plan_t;
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, inconsistent descriptor */
-  ATTN_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+  ATTN_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement */
   ATTN_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed */
   ATTN_ERR_HIP = 4               /* a HIP runtime call failed */
 } attn_status_t;

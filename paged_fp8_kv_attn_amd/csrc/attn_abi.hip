@@ -102,7 +102,7 @@ const char* attn_status_string(attn_status_t s) {
   switch (s) {
     case ATTN_OK: return "ATTN_OK: success";
     case ATTN_ERR_INVALID_ARGUMENT: return "ATTN_ERR_INVALID_ARGUMENT: null/misaligned pointer or inconsistent descriptor";
-    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: request outside what this build implements";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: request outside what this library implements";
     case ATTN_ERR_OUT_OF_MEMORY: return "ATTN_ERR_OUT_OF_MEMORY: workspace allocation failed";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: a HIP runtime call failed (see attn_last_hip_error)";
   }
