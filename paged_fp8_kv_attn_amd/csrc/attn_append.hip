@@ -221,6 +221,24 @@ __global__ __launch_bounds__(64 * kAppendWaves) void kv_append_kernel(AppendPara
   amax = wave_max(amax);
   const float scale = (amax == 0.f) ? 1.f : amax / (KI8 ? 127.f : 448.f);
   const bool changed = n_old == 0 || __float_as_uint(scale) != __float_as_uint(old_scale);
+  // value / scale, correctly rounded, without a full division per value:
+  // y = 1/scale is correctly rounded (one IEEE division per wave); q0 = x y
+  // is within two ulps of x / scale; one fma correction makes it faithful,
+  // and a second gives the correctly rounded quotient (Markstein's theorem:
+  // a correctly rounded reciprocal and a faithful quotient).  The residuals
+  // x - q scale are exact fmas and stay normal for scales in [2^-90, 2^90];
+  // other scales take the IEEE division.
+  const bool fast_div = scale >= 0x1p-90f && scale <= 0x1p90f;
+  const float rcp = 1.f / scale;
+  auto quot = [&](float x) -> float {
+    if (!fast_div) return x / scale;
+    const float q0 = x * rcp;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, scale, x), rcp, q0);
+    const float q2 = __builtin_fmaf(__builtin_fmaf(-q1, scale, x), rcp, q1);
+    // the scale is positive, so the quotient has x's sign; the corrections
+    // would turn a -0 quotient into +0 (-0 + +0 is +0)
+    return __builtin_copysignf(q2, x);
+  };
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -235,7 +253,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void kv_append_kernel(AppendPara
     for (int q = 0; q < 4; ++q) {
       float y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = val[u][4 * q + e] / scale;
+      for (int e = 0; e < 4; ++e) y[e] = quot(val[u][4 * q + e]);
       const uint32_t enc = KI8 ? f32x4_to_i8x4(y[0], y[1], y[2], y[3]) : f32x4_to_fp8x4(y[0], y[1], y[2], y[3]);
       // bytes of slots at or past the new length keep their old value
       uint32_t keep = 0u;

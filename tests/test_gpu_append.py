@@ -105,3 +105,37 @@ def test_append_cases_int8(idx):
     ql, cl, hkv, d, dt, sig = CASES[idx]
     _append_parity(sa.append_case(ql, cl, num_kv_heads=hkv, head_dim=d, new_dtype=dt, seed=90 + idx,
                                   new_sigmas=sig, name=f"append_int8_edge{idx}", kv_format="int8"))
+
+
+@pytest.mark.parametrize("kv_format", ["e4m3", "int8"])
+def test_append_quotients_at_rounding_midpoints(kv_format):
+    # fresh pages whose values, divided by the page scale, land on (and one
+    # or two fp32 ulps beside) every rounding midpoint of the format, so that
+    # any quotient not rounded exactly as IEEE fp32 division changes a byte
+    rng = np.random.default_rng(7 if kv_format == "e4m3" else 8)
+    qmax = 448.0 if kv_format == "e4m3" else 127.0
+    if kv_format == "e4m3":
+        vals = e4m3.decode(np.arange(0x7F, dtype=np.uint8))
+        mids = (vals[:-1] + vals[1:]) / 2
+    else:
+        mids = np.arange(-127, 127) + 0.5
+    B, D, S = 12, 128, 16
+    c = sa.append_case([S] * B, [S] * B, num_kv_heads=1, head_dim=D, new_dtype="f32", seed=70, kv_format=kv_format,
+                       name=f"append_midpoints_{kv_format}")
+    f32 = np.float32
+    for which, tens in ((0, c.k_new), (1, c.v_new)):
+        x = np.empty((B * S, 1, D), dtype=f32)
+        for b in range(B):
+            s0 = f32(np.exp(rng.uniform(np.log(1e-3), np.log(50.0))))
+            xmax = f32(s0 * f32(qmax))
+            scale = f32(xmax / f32(qmax))  # the scale the append will compute
+            m = rng.choice(mids, size=S * D)
+            m = m * rng.choice([-1.0, 1.0], size=m.size) if kv_format == "e4m3" else m
+            q = np.nextafter(m.astype(f32), np.where(rng.random(m.size) < 0.5, f32(-1e9), f32(1e9)))
+            q = np.where(rng.random(m.size) < 0.4, m.astype(f32), q)
+            vals_b = (q.astype(np.float64) * np.float64(scale)).astype(f32)
+            vals_b = np.clip(vals_b, -xmax, xmax)
+            vals_b[0] = xmax
+            x[b * S:(b + 1) * S, 0, :] = vals_b.reshape(S, D)
+        tens.copy_(torch.from_numpy(x))
+    _append_parity(c)
