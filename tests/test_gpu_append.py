@@ -78,6 +78,8 @@ CASES = [
     ([5, 5, 5], [5, 133, 700], 8, 128, "bf16", (0.5, 2.0)),  # MTP-shaped appends
     ([64, 33, 16], [64, 40, 1000], 2, 128, "f32", (1.0, 8.0)),
     ([16], [16], 1, 64, "f32", (0.0,)),  # all-zero rows: scale 1
+    ([16, 5], [16, 5], 1, 64, "f32", (1e-30,)),  # page scales below 2^-90: plain IEEE division
+    ([16, 9], [16, 9], 1, 128, "f32", (1e30,)),  # page scales above 2^90
 ]
 
 
