@@ -109,7 +109,8 @@ def append_config(c) -> dict:
         "ctx_min": int(c.ctx_lens.min()),
         "ctx_max": int(c.ctx_lens.max()),
         "new_dtype": c.new_dtype,
-        "kv_format": "fp8_e4m3 (OCP), fp32 scale per (page, kv head)",
+        "kv_format": ("int8 (two's complement), fp32 scale per (page, kv head)" if c.kv_format == "int8"
+                      else "fp8_e4m3 (OCP), fp32 scale per (page, kv head)"),
         "seed": c.seed,
     }
 
@@ -124,7 +125,7 @@ def append_cpu_baseline(c, counts, budget_s: float) -> dict:
     calls = 0
     while True:
         oracle.paged_kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.kv_scales, c.block_table, c.ctx_lens,
-                               c.q_lens)
+                               c.q_lens, kv_format=c.kv_format)
         calls += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -457,12 +458,12 @@ def main():
         def __init__(self, name):
             from synth.append import make_append_case
 
-            c = make_append_case(name)
+            c = make_append_case(name, kv_format=args.kv_format)
             self.w = c
             self.counts = append_counts(c)
             self.plan = Plan(num_seqs=c.num_seqs, num_q_heads=c.num_kv_heads, num_kv_heads=c.num_kv_heads,
                              head_dim=c.head_dim, num_pages=c.num_pages, max_pages_per_seq=c.max_pages_per_seq,
-                             max_q_len=c.max_q_len, max_ctx_len=c.max_ctx_len)
+                             max_q_len=c.max_q_len, max_ctx_len=c.max_ctx_len, kv_format=c.kv_format)
             self.k_new = c.k_new.to(dev).contiguous()
             self.v_new = c.v_new.to(dev).contiguous()
             self.bt = t(c.block_table)
@@ -659,7 +660,7 @@ def main():
         res["parts"] = [{"workload": pt.w.name, "roofline": roofline(pt, committed_traffic(profile_name(pt.w), pt.kernel))}
                         for pt in parts]
     if args.workload in APPEND_WORKLOADS:
-        res["dtype"] = "f32 (IEEE divide) -> fp8 e4m3"
+        res["dtype"] = "f32 (correctly rounded divide) -> " + ("int8" if args.kv_format == "int8" else "fp8 e4m3")
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = append_cpu_baseline(dom.w, dom.counts, args.cpu_seconds)
     elif args.workload in ACCEPT_WORKLOADS:

@@ -133,7 +133,8 @@ APPEND_CONFIGS = {"append_decode": dict(seed=12), "append_prefill": dict(seed=15
 
 
 def make_append_case(name: str, seed: int | None = None, *, batch: int | None = None,
-                     ctx_range: tuple | None = None, new_dtype: str = "bf16", q_len: int | None = None) -> AppendCase:
+                     ctx_range: tuple | None = None, new_dtype: str = "bf16", q_len: int | None = None,
+                     kv_format: str = "e4m3") -> AppendCase:
     if name not in APPEND_CONFIGS:
         raise KeyError(name)
     seed = APPEND_CONFIGS[name]["seed"] if seed is None else seed
@@ -153,7 +154,7 @@ def make_append_case(name: str, seed: int | None = None, *, batch: int | None = 
         q = np.full(B, chunk, np.int32)
         mpps = (hi + chunk + PAGE_SIZE - 1) // PAGE_SIZE
     return append_case(q, ctx, num_kv_heads=8, head_dim=128, new_dtype=new_dtype,
-                       seed=int(rng.integers(0, 2**31)), max_pages_per_seq=mpps, name=name)
+                       seed=int(rng.integers(0, 2**31)), max_pages_per_seq=mpps, name=name, kv_format=kv_format)
 
 
 __all__ = ["AppendCase", "append_case", "make_append_case", "APPEND_CONFIGS", "POISON_BYTE"]
