@@ -115,6 +115,18 @@ def append_config(c) -> dict:
     }
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def append_cpu_baseline(c, counts, budget_s: float) -> dict:
     """Time the append oracle (as it stands) on the host over whole calls."""
     import oracle
@@ -179,7 +191,7 @@ def accept_cpu_baseline(c, counts, budget_s: float) -> dict:
     return {"value": counts["bytes"] * calls / wall / 1e9, "unit": "GB/s",
             "cores": max(1, int(math.ceil(cpu / wall - 0.05))), "kind": "oracle",
             "sample": (f"{calls} whole acceptance calls of the same workload, {wall:.1f} s wall, {cpu:.1f} s CPU "
-                       f"on {ncpu} allowed threads; numpy oracle"), "threads_allowed": ncpu}
+                       f"on {ncpu} allowed threads; numpy oracle"), "threads_allowed": ncpu, "cpu_model": cpu_model()}
 
 
 def workload_config(w) -> dict:
@@ -370,6 +382,7 @@ def cpu_baseline(w, counts, budget_s: float) -> dict:
                    f"{done_tokens / wall:.1f} query-tokens/s"),
         "query_tokens_per_s": done_tokens / wall,
         "threads_allowed": ncpu,
+        "cpu_model": cpu_model(),
     }
 
 
