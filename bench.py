@@ -152,6 +152,7 @@ def append_cpu_baseline(c, counts, budget_s: float) -> dict:
         "sample": (f"{calls} whole append calls of the same workload (copying the pools each call), {wall:.1f} s "
                    f"wall, {cpu:.1f} s CPU on {ncpu} allowed threads; numpy oracle"),
         "threads_allowed": ncpu,
+        "cpu_model": cpu_model(),
     }
 
 
