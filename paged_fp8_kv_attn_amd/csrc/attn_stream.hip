@@ -1659,6 +1659,9 @@ static const void* kernel_tiles(const Variant& v) {
   if (v.tile_waves == 2 && v.col_tiles == 1) return tile_d<D, 2, 1>(v);
   if (v.tile_waves == 4 && v.col_tiles == 1) return tile_d<D, 4, 1>(v);
   if (v.tile_waves == 4 && v.col_tiles == 2) return tile_d<D, 4, 2>(v);
+  if constexpr (D == 128) {
+    if (v.tile_waves == 8 && v.col_tiles == 2) return tile_d<D, 8, 2>(v);
+  }
   if (v.tile_waves != 0 || v.col_tiles != 1) return nullptr;
   return v.dup_lo ? kernel_d<D, 1, true>(v) : kernel_d<D, 1, false>(v);
 }
