@@ -1691,15 +1691,17 @@ hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int 
   return hipLaunchKernel(f, dim3(grid), dim3(64 * waves_per_group(v)), args, 0, stream);
 }
 
-// Columns per merge workgroup: one for blocks of at most 4 columns (decode)
-// and when segments have many pieces (expected_parts per segment: a
-// column's pieces then spread over up to NG / C thread groups), else as
-// many as the NG = 256 / (D/4) thread groups cover.
+// Columns per merge workgroup: one for blocks of at most 4 columns (decode);
+// otherwise the NG = 256 / (D/4) thread groups are spread over a column's
+// pieces (expected_parts per segment) so that each group still merges two
+// or more of them, and the rest of the groups take further columns.  (On
+// 64-column MQA blocks with ~8 pieces, two columns per workgroup measured
+// faster than one column over all eight groups or eight columns of one.)
 int merge_cols_for(const Variant& v, int cols_per_block, int64_t expected_parts) {
   if (cols_per_block <= 4) return 1;
   const int ng = kMergeThreads / (v.head_dim / 4);
   int spread = 1;
-  while (spread < expected_parts && spread < ng) spread <<= 1;
+  while (2 * spread < expected_parts && spread < ng) spread <<= 1;
   return ng / spread;
 }
 
