@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import resource
 import sys
 import time
@@ -216,10 +217,25 @@ def workload_config(w) -> dict:
 
 
 def source_hash(path: str = KERNEL_SOURCE) -> str:
-    """Hash of a kernel's source, so a counter summary taken on an older
-    kernel is not applied to a newer one."""
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel's source and of the local headers it includes
+    (``#include "..."``, followed transitively), so a counter summary taken
+    on an older kernel is not applied to a newer one."""
+    h = hashlib.sha256()
+    seen = set()
+
+    def add(fp: str):
+        fp = os.path.normpath(fp)
+        if fp in seen:
+            return
+        seen.add(fp)
+        with open(fp, "rb") as f:
+            data = f.read()
+        h.update(data)
+        for m in re.finditer(rb'^\s*#\s*include\s+"([^"]+)"', data, re.M):
+            add(os.path.join(os.path.dirname(fp), m.group(1).decode()))
+
+    add(path)
+    return h.hexdigest()[:16]
 
 
 def attention_kernel_name(info: dict) -> str:

@@ -78,15 +78,13 @@ __device__ __forceinline__ f32x4 fp8x4_to_f32x4(uint32_t w) {
   return f32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// Four INT8 bytes (two's complement) -> four bf16, exactly: byte b becomes
-// the fp32 value 2^23 + (b XOR 0x80) (its bits 0x4B0000uu), minus 2^23 + 128,
-// and every integer in [-128, 127] is a bf16 value.
+// Four INT8 bytes (two's complement) -> four bf16, exactly: each byte is
+// sign-extended and converted to fp32 (one v_cvt_f32_i32 with an SDWA byte
+// select each), and every integer in [-128, 127] is a bf16 value.
 __device__ __forceinline__ bf16x4 i8x4_to_bf16x4(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
   float f[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    f[e] = __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, u, 0x070C0C00u | (uint32_t)e)) - 8388736.0f;
+  for (int e = 0; e < 4; ++e) f[e] = (float)(int)(int8_t)(uint8_t)(w >> (8 * e));
   const bf16x2 a = __builtin_convertvector(f32x2{f[0], f[1]}, bf16x2);
   const bf16x2 b = __builtin_convertvector(f32x2{f[2], f[3]}, bf16x2);
   return bf16x4{a[0], a[1], b[0], b[1]};

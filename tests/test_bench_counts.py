@@ -81,3 +81,16 @@ def test_traffic_scaled_by_the_copy_and_dropped_for_another_source(tmp_path, mon
     _summary(tmp_path, "0000000000000000", 1000.0, 10.0, float(1 << 21))
     assert bench.committed_traffic("demo") is None
     assert bench.committed_traffic("absent") is None
+
+
+def test_source_hash_follows_local_includes(tmp_path):
+    (tmp_path / "k.hip").write_text('#include <hip/hip_runtime.h>\n#include "a.h"\n__global__ void k() {}\n')
+    (tmp_path / "a.h").write_text('#include "b.h"\n#include "a.h"\n')  # a cycle is followed once
+    (tmp_path / "b.h").write_text("constexpr int kB = 1;\n")
+    h0 = bench.source_hash(str(tmp_path / "k.hip"))
+    assert h0 == bench.source_hash(str(tmp_path / "k.hip"))
+    (tmp_path / "b.h").write_text("constexpr int kB = 2;\n")  # a change two includes down
+    h1 = bench.source_hash(str(tmp_path / "k.hip"))
+    assert h1 != h0
+    (tmp_path / "b.h").write_text("constexpr int kB = 1;\n")
+    assert bench.source_hash(str(tmp_path / "k.hip")) == h0
