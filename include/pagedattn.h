@@ -274,6 +274,13 @@ attn_status_t attn_debug_gather(attn_plan_t plan, const uint8_t* k_pages, const 
  * (FP8 -> bf16, widened exactly to fp32).  n >= 0; n == 0 enqueues nothing. */
 attn_status_t attn_debug_decode_fp8(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
 
+/* out[i] = the value of INT8 byte in[i] (two's complement) as the attention
+ * kernels widen it for ATTN_KV_INT8 pools (byte -> bf16, widened exactly to
+ * fp32; the page scale is not applied).  in: n bytes, out: n floats, both
+ * device memory, out 4-byte aligned.  n >= 0; n == 0 enqueues nothing;
+ * n < 0 or a null pointer -> ATTN_ERR_INVALID_ARGUMENT. */
+attn_status_t attn_debug_decode_int8(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
+
 /* out[i] = the E4M3 byte of fp32 in[i] as the append kernel encodes it
  * (nearest code, ties to even, magnitudes above 448 saturated, sign kept;
  * finite inputs).  n >= 0; n == 0 enqueues nothing. */

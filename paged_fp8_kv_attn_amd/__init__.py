@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     Plan,
     PlanInfo,
     debug_decode_fp8,
+    debug_decode_int8,
     debug_encode_fp8,
     debug_gather,
     exported_symbols,

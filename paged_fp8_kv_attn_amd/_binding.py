@@ -29,6 +29,7 @@ _FUNCTIONS = [
     "attn_last_hip_error",
     "attn_debug_gather",
     "attn_debug_decode_fp8",
+    "attn_debug_decode_int8",
     "attn_kv_append",
     "attn_debug_encode_fp8",
     "attn_mtp_accept_workspace_size",
@@ -122,6 +123,8 @@ def load_library():
     lib.attn_debug_gather.restype = i32
     lib.attn_debug_decode_fp8.argtypes = [vp, vp, i64, vp]
     lib.attn_debug_decode_fp8.restype = i32
+    lib.attn_debug_decode_int8.argtypes = [vp, vp, i64, vp]
+    lib.attn_debug_decode_int8.restype = i32
     lib.attn_kv_append.argtypes = [vp, vp, vp, i32] + [vp] * 7
     lib.attn_kv_append.restype = i32
     lib.attn_debug_encode_fp8.argtypes = [vp, vp, i64, vp]
@@ -258,6 +261,12 @@ def debug_gather(plan: Plan, k_pages, v_pages, kv_scales, block_table, ctx_lens,
 def debug_decode_fp8(codes, out, stream=None):
     st = load_library().attn_debug_decode_fp8(_ptr(codes), _ptr(out), int(codes.numel()), _stream(stream))
     _check(st, "attn_debug_decode_fp8")
+    return out
+
+
+def debug_decode_int8(codes, out, stream=None):
+    st = load_library().attn_debug_decode_int8(_ptr(codes), _ptr(out), int(codes.numel()), _stream(stream))
+    _check(st, "attn_debug_decode_int8")
     return out
 
 

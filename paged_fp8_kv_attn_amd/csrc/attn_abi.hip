@@ -473,7 +473,15 @@ attn_status_t attn_debug_decode_fp8(const uint8_t* in, float* out, int64_t n, hi
   if (n < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (n == 0) return ATTN_OK;
   if (!in || !out || !aligned(out, 4)) return ATTN_ERR_INVALID_ARGUMENT;
-  const hipError_t e = pa::launch_debug_decode(in, out, n, stream);
+  const hipError_t e = pa::launch_debug_decode(in, out, n, false, stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+attn_status_t attn_debug_decode_int8(const uint8_t* in, float* out, int64_t n, hipStream_t stream) {
+  if (n < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (n == 0) return ATTN_OK;
+  if (!in || !out || !aligned(out, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  const hipError_t e = pa::launch_debug_decode(in, out, n, true, stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

@@ -1,6 +1,6 @@
-// Checking hooks: the block-table gather and the FP8 decode, run with the
-// same device helpers (chunk_offset, k_in_chunk, v_in_chunk,
-// fp8x8_to_bf16x8) as the attention kernels.
+// Checking hooks: the block-table gather and the FP8 and INT8 decodes, run
+// with the same device helpers (chunk_offset, k_in_chunk, v_in_chunk,
+// kv8x8_to_bf16x8) as the attention kernels.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -47,13 +47,14 @@ __global__ __launch_bounds__(256) void debug_gather_kernel(GatherParams p) {
   }
 }
 
-// one thread per 8 input bytes
+// one thread per 8 input bytes: E4M3 codes, or INT8 with KI8
+template <bool KI8>
 __global__ __launch_bounds__(256) void debug_decode_kernel(const uint8_t* in, float* out, int64_t n) {
   const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (i0 >= n) return;
   uint32_t w[2] = {0u, 0u};
   for (int k = 0; k < 8 && i0 + k < n; ++k) w[k / 4] |= (uint32_t)in[i0 + k] << (8 * (k % 4));
-  const bf16x8 v = fp8x8_to_bf16x8(w[0], w[1]);
+  const bf16x8 v = kv8x8_to_bf16x8<KI8>(w[0], w[1]);
   for (int k = 0; k < 8 && i0 + k < n; ++k) out[i0 + k] = (float)v[k];
 }
 
@@ -66,12 +67,15 @@ hipError_t launch_debug_gather(const GatherParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, hipStream_t stream) {
+hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, bool kv_int8, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t threads = (n + 7) / 8;
   const int64_t blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(debug_decode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
+  if (kv_int8)
+    hipLaunchKernelGGL(debug_decode_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
+  else
+    hipLaunchKernelGGL(debug_decode_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
   return hipGetLastError();
 }
 

@@ -133,6 +133,6 @@ hipError_t launch_mtp_accept(const AcceptParams& p, bool f32, hipStream_t stream
                              hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_debug_gather(const GatherParams& p, hipStream_t stream);
-hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
+hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, bool kv_int8, hipStream_t stream);
 
 }  // namespace pa

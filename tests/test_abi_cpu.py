@@ -79,6 +79,9 @@ def test_null_arguments_rejected():
     assert lib.attn_debug_decode_fp8(None, None, -1, None) == 1
     assert lib.attn_debug_decode_fp8(None, None, 0, None) == 0
     assert lib.attn_debug_decode_fp8(None, None, 5, None) == 1
+    assert lib.attn_debug_decode_int8(None, None, -1, None) == 1
+    assert lib.attn_debug_decode_int8(None, None, 0, None) == 0
+    assert lib.attn_debug_decode_int8(None, None, 5, None) == 1
     assert lib.attn_kv_append(None, None, None, 1, *([None] * 7)) == 1
     assert lib.attn_debug_encode_fp8(None, None, -1, None) == 1
     assert lib.attn_debug_encode_fp8(None, None, 0, None) == 0

@@ -1,11 +1,13 @@
-"""GPU checks of the shared device helpers, bit for bit: the FP8 decode over
-all 256 codes and the block-table gather (bytes, scales, page ids)."""
+"""GPU checks of the shared device helpers, bit for bit: the FP8 and INT8
+decodes over all 256 codes and the block-table gather (bytes, scales, page
+ids)."""
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import oracle.attention as oracle_attention
 import paged_fp8_kv_attn_amd as pa
 from synth import custom_workload, make_workload
 from tests.gpu_helpers import device_inputs, log, plan_for
@@ -27,6 +29,20 @@ def test_decode_all_codes_bit_exact():
         assert np.array_equal(np.isnan(got), nan)
         assert np.array_equal(got[~nan], ref[~nan])
         assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_int8_decode_all_codes_bit_exact():
+    log("int8 decode: 256 codes x 3 (contiguous, ragged length)")
+    codes = torch.arange(256, dtype=torch.uint8).repeat(3)
+    for n in (768, 767, 5):
+        c = codes[:n].cuda()
+        out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+        pa.debug_decode_int8(c, out)
+        torch.cuda.synchronize()
+        got = out.double().cpu().numpy()
+        ref = oracle_attention.decode_int8(codes[:n].numpy())
+        assert np.array_equal(got, ref)
+        assert not np.any(np.signbit(got[ref == 0]))  # code 0 widens to +0
 
 
 @pytest.mark.parametrize("case", ["tiny", "ragged", "llama_reduced", "d64_mqa"])
