@@ -120,11 +120,20 @@ __device__ __forceinline__ int seg_chunks(int L, int Q, int G, int cpb, int cb) 
   return (L - Q + i_hi + 1 + kChunk - 1) / kChunk;
 }
 
-// Chunks of one kv head of a sequence: all of its column blocks.
+// What a segment counts for in the balanced split: its chunks, plus
+// p.start_cost for its start, and nothing without chunks.  Position v of a
+// segment's count is its chunk v - start_cost (none for v < start_cost).
+__device__ __forceinline__ int sched_chunks(const StreamParams& p, int L, int Q, int cb) {
+  const int n = seg_chunks(L, Q, p.group, p.cols_per_block, cb);
+  return n > 0 ? n + p.start_cost : 0;
+}
+
+// Count of one kv head of a sequence in the balanced split: all of its
+// column blocks.
 __device__ __forceinline__ int head_chunks(const StreamParams& p, int L, int Q) {
-  if (p.col_blocks == 1) return seg_chunks(L, Q, p.group, p.cols_per_block, 0);
+  if (p.col_blocks == 1) return sched_chunks(p, L, Q, 0);
   int s = 0;
-  for (int cb = 0; cb < p.col_blocks; ++cb) s += seg_chunks(L, Q, p.group, p.cols_per_block, cb);
+  for (int cb = 0; cb < p.col_blocks; ++cb) s += sched_chunks(p, L, Q, cb);
   return s;
 }
 
@@ -1400,11 +1409,11 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
   int h = (int)(off / per_head);
   int r = (int)(off - (int64_t)h * per_head);
   int cb = 0;
-  int n = seg_chunks(L, Q, p.group, p.cols_per_block, 0);
+  int n = sched_chunks(p, L, Q, 0);
   while (r >= n) {
     r -= n;
     ++cb;
-    n = seg_chunks(L, Q, p.group, p.cols_per_block, cb);
+    n = sched_chunks(p, L, Q, cb);
   }
   int64_t cur = lo;
   while (true) {
@@ -1416,8 +1425,11 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
     pc.L = L;
     pc.Q = Q;
     pc.row0 = row0;
-    pc.c_begin = r;
-    pc.c_end = r + take;
+    // positions [r, r + take) of the segment's count: its chunks from
+    // r - start_cost (a piece holding only the start position has none and
+    // writes an empty partial: max -inf, sum 0)
+    pc.c_begin = max(r - p.start_cost, 0);
+    pc.c_end = max(r + take - p.start_cost, 0);
     pc.whole = (r == 0) && (take == n);
     const int seg = (b * p.num_kv_heads + h) * p.col_blocks + cb;
     pc.slot = seg + w;
@@ -1442,7 +1454,7 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
           Q = p.q_lens[b];
         }
       }
-      n = seg_chunks(L, Q, p.group, p.cols_per_block, cb);
+      n = sched_chunks(p, L, Q, cb);
     } while (n == 0);
   }
 }
