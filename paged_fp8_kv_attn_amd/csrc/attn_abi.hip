@@ -244,8 +244,9 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   // batch-32 decode shape, splits in which a quarter of the waves do so ran
   // 31.6-32.3 us against 30.0-30.2 us for the same bytes with none.  The
   // balanced split counts each segment start as one chunk, so those waves
-  // stream one chunk less.
-  p->start_cost = v.packed ? 1 : 0;
+  // stream one chunk less.  A forced split count keeps its exact cut: n
+  // equal pieces of every segment.
+  p->start_cost = (v.packed && d.num_kv_splits == 0) ? 1 : 0;
   p->grid = static_cast<int>(ceil_div(units * unit_waves, wpg));
   // merge: one workgroup per segment (and slice of its columns); segments
   // with many pieces on average get fewer columns per workgroup
