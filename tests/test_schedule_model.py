@@ -1,0 +1,106 @@
+"""The balanced chunk schedule that the attention kernels walk, written out
+on the CPU and checked against what the merge relies on (CPU only).
+
+The kernels give unit w of W the positions [floor(wT/W), floor((w+1)T/W))
+of the concatenated segment counts, a segment counting its chunks plus a
+start cost; position v of a segment is its chunk v - start_cost.  Every
+real chunk must be covered exactly once, every (segment, unit) piece must
+have its own partial slot (segment + w), the unit holding a segment's start
+must record its first slot and the number of pieces, and a segment held by
+one unit is written whole."""
+
+import itertools
+import random
+
+import pytest
+
+
+def _wg_of_chunk(g, T, W):
+    return ((g + 1) * W + T - 1) // T - 1
+
+
+def _walk(real, w_max, min_chunks, start_cost):
+    sched = [n + start_cost if n > 0 else 0 for n in real]
+    T = sum(sched)
+    W = max(1, min(w_max, T // min_chunks))
+    starts = [0] + list(itertools.accumulate(sched))
+    pieces = {s: [] for s in range(len(real))}
+    merge = {}
+    for w in range(W):
+        lo, hi = w * T // W, (w + 1) * T // W
+        if lo >= hi:
+            continue
+        s = next(i for i in range(len(real)) if sched[i] > 0 and starts[i] <= lo < starts[i] + sched[i])
+        r, cur = lo - starts[s], lo
+        while True:
+            n = sched[s]
+            take = min(n - r, hi - cur)
+            whole = r == 0 and take == n
+            pieces[s].append((w, max(r - start_cost, 0), max(r + take - start_cost, 0), whole))
+            if r == 0:
+                merge[s] = (s + w, 1 if whole else _wg_of_chunk(cur + n - 1, T, W) - w + 1)
+            cur += take
+            if cur >= hi:
+                break
+            r = 0
+            s += 1
+            while sched[s] == 0:
+                s += 1
+    return pieces, merge
+
+
+def _check(real, w_max, min_chunks, start_cost):
+    if sum(real) == 0:
+        return
+    pieces, merge = _walk(real, w_max, min_chunks, start_cost)
+    slots = set()
+    for s, n in enumerate(real):
+        ps = pieces[s]
+        if n == 0:
+            assert not ps
+            continue
+        cover = [0] * n
+        for w, cb, ce, _ in ps:
+            assert 0 <= cb <= ce <= n
+            for c in range(cb, ce):
+                cover[c] += 1
+            assert s + w not in slots
+            slots.add(s + w)
+        assert cover == [1] * n, (real, s, ps)
+        first, count = merge[s]
+        assert first == s + ps[0][0] and count == len(ps)
+        assert [p[0] for p in ps] == list(range(ps[0][0], ps[0][0] + count))
+        if count == 1:
+            assert ps[0][3] and ps[0][1:3] == (0, n)
+        else:
+            assert not any(p[3] for p in ps)
+        assert any(ce > cb for _, cb, ce, _ in ps)  # some unit reads the segment
+
+
+@pytest.mark.parametrize("start_cost", [0, 1, 2])
+def test_schedule_random_mixes(start_cost):
+    rng = random.Random(100 + start_cost)
+    for _ in range(600):
+        real = [rng.choice([0, rng.randint(1, 3), rng.randint(1, 200)]) for _ in range(rng.randint(1, 40))]
+        _check(real, rng.choice([1, 2, 7, 64, 1024]), rng.choice([1, 2, 8]), start_cost)
+
+
+def test_schedule_decode_shapes():
+    # 32 sequences x 8 kv heads: aligned lengths, alternating lengths, one long one
+    for real in ([72] * 256, [70] * 8 + [74] * 8, [1] * 255 + [4000]):
+        for sc in (0, 1):
+            _check(real * (256 // len(real)) if len(real) < 256 else real, 1024, 8, sc)
+
+
+def test_empty_start_piece_is_possible_and_covered():
+    # with a start cost a unit can hold only a segment's start position: its
+    # piece has no chunks (the kernel writes an empty partial for it)
+    found = False
+    rng = random.Random(7)
+    for _ in range(300):
+        real = [rng.randint(1, 30) for _ in range(rng.randint(2, 12))]
+        pieces, _ = _walk(real, 64, 1, 1)
+        if any(cb == ce for ps in pieces.values() for _, cb, ce, _ in ps):
+            found = True
+            _check(real, 64, 1, 1)
+    assert found
