@@ -244,9 +244,11 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   // kernels also the LDS staging): on the batch-32 decode shape, splits in
   // which a quarter of the waves do so ran 31.6-32.3 us against 30.0-30.2 us
   // for the same bytes with none.  The balanced split counts each segment
-  // start as one chunk, so those units stream one chunk less.  A forced
-  // split count keeps its exact cut: n equal pieces of every segment.
-  p->start_cost = d.num_kv_splits == 0 ? 1 : 0;
+  // start as chunks, so those units stream that much less: one for the
+  // packed decode, two for the tile kernel, whose restart also refills its
+  // ring and LDS staging (measured best of 0-2 on each).  A forced split
+  // count keeps its exact cut: n equal pieces of every segment.
+  p->start_cost = d.num_kv_splits != 0 ? 0 : (v.packed ? 1 : 2);
   p->grid = static_cast<int>(ceil_div(units * unit_waves, wpg));
   // merge: one workgroup per segment (and slice of its columns); segments
   // with many pieces on average get fewer columns per workgroup
