@@ -281,6 +281,123 @@ def committed_traffic(workload: str, kernel: str = "attn_stream_kernel"):
     return fetch * (copy_bytes / cf) + write * (copy_bytes / cw)
 
 
+STREAM_CEILING = os.path.join(PROFILES, "stream_read_ceiling.txt")
+
+
+def committed_sq_counters(workload: str, kernel: str):
+    """MFMA and VALU busy fractions of the attention kernel from the committed
+    rocprofv3 SQ counter summary, if it was taken on the current kernel
+    source; otherwise None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_sq_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_hash(KERNEL_SOURCE):
+        return None
+    try:
+        return {"mfma_busy_frac": float(vals["mfma_busy_frac"]), "valu_busy_frac": float(vals["valu_busy_frac"]),
+                "coexec_frac_of_mfma_busy": float(vals["coexec_frac_of_mfma_busy"]),
+                "source": os.path.relpath(path, ROOT)}
+    except (KeyError, ValueError):
+        return None
+
+
+def committed_stream_ceiling(w):
+    """The measured streaming-read ceiling for chunks of one (page, kv head)
+    of the workload (16 * head_dim bytes: 2 KB at D = 128), from the
+    committed calibration summary; None when it has no such line."""
+    if not os.path.exists(STREAM_CEILING) or not hasattr(w, "head_dim"):
+        return None
+    want = 16 * w.head_dim
+    with open(STREAM_CEILING) as f:
+        for line in f:
+            if line.startswith("chunk_bytes"):
+                parts = dict(kv.split("=") for kv in line.split())
+                if int(parts["chunk_bytes"]) == want:
+                    return {"GB/s": float(parts["best_GBps"]), "chunk_bytes": want,
+                            "source": "profiles/stream_read_ceiling.txt"}
+    return None
+
+
+def stream_calibration(dev, args):
+    """Streaming-read ceiling: random distinct chunks of a 2 GiB pool, 1-64 KB
+    each, ~150 MB per launch (the batch-32 decode's KV bytes), read by the
+    library's attn_calib_stream_read; each repetition reads another slice of
+    a random permutation of the pool's chunks, so no chunk is read twice in
+    a row and the 256 MB Infinity Cache cannot hold what the next launch
+    reads.  Also a contiguous read of the same size (ids in order)."""
+    import torch
+
+    from paged_fp8_kv_attn_amd import calib_stream_read, load_library
+
+    load_library()
+    pool_bytes = 2 << 30
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    pool.fill_(0x5A)
+    target = 150_000_000
+    reps = max(5, args.reps)
+    rng = np.random.default_rng(7)
+    rows = []
+    hipt = HipGraph()
+    for chunk in (1024, 2048, 4096, 8192, 16384, 65536):
+        nchunks = target // chunk
+        pool_chunks = pool_bytes // chunk
+        perm = rng.permutation(pool_chunks).astype(np.int32)
+        for order in ("random", "sequential"):
+            if order == "sequential" and chunk != 65536:
+                continue
+            for waves in (1024, 2048, 4096):
+                sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+                times = []
+                for r in range(reps + 1):
+                    if order == "random":
+                        lo = (r * nchunks) % (pool_chunks - nchunks)
+                        ids = torch.from_numpy(perm[lo:lo + nchunks].copy()).to(dev)
+                    else:
+                        start = (r * nchunks) % (pool_chunks - nchunks)
+                        ids = torch.arange(start, start + nchunks, dtype=torch.int32, device=dev)
+                    a, b = hipt.event(), hipt.event()
+                    torch.cuda.synchronize()
+                    calib_stream_read(pool, ids, chunk, waves, sink, kernel_events=(a, b))
+                    torch.cuda.synchronize()
+                    if r > 0:  # the first launch is a warm-up
+                        times.append(hipt.elapsed_ms(a, b))
+                    hipt.destroy_event(a)
+                    hipt.destroy_event(b)
+                med = float(np.median(times))
+                rows.append({"chunk_bytes": chunk, "order": order, "waves": waves, "bytes": nchunks * chunk,
+                             "median_us": med * 1e3, "GBps": nchunks * chunk / (med * 1e-3) / 1e9,
+                             "min_us": float(np.min(times)) * 1e3, "max_us": float(np.max(times)) * 1e3})
+                print(json.dumps(rows[-1]), flush=True)
+    best = {}
+    for r in rows:
+        key = (r["chunk_bytes"], r["order"])
+        if key not in best or r["GBps"] > best[key]["GBps"]:
+            best[key] = r
+    if args.summary_out:
+        lines = ["# Streaming-read ceiling on MI355X (gfx950): attn_calib_stream_read reading distinct random",
+                 "# chunks of a 2 GiB pool (a different slice of one random permutation per launch), ~150 MB per",
+                 "# launch, 16-byte non-temporal loads, 16 lines of 1 KB in flight per wave, waves streaming equal",
+                 "# contiguous shares of the chunk list; the best of 1024/2048/4096 waves, median of "
+                 f"{reps} launches",
+                 "# timed with HIP events attached to the kernel's dispatch.  'sequential' reads consecutive chunks.",
+                 "# command: python bench.py --stream-calibration --summary-out profiles/stream_read_ceiling.txt"]
+        for (chunk, order), r in sorted(best.items()):
+            tag = "chunk_bytes" if order == "random" else "sequential_chunk_bytes"
+            lines.append(f"{tag}={chunk} best_GBps={r['GBps']:.1f} waves={r['waves']} median_us={r['median_us']:.2f} "
+                         f"bytes={r['bytes']}")
+        lines.append("# all runs:")
+        lines += ["# " + json.dumps(r) for r in rows]
+        with open(args.summary_out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+    print(json.dumps({"stream_ceiling": {f"{c}_{o}": round(r["GBps"], 1) for (c, o), r in sorted(best.items())}}))
+
+
 class HipGraph:
     """A HIP graph captured in global capture mode straight through the HIP
     runtime (only library calls run inside the capture), so that the event
@@ -408,12 +525,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--reps", type=int, default=5,
+                    help="timed repetitions of the K steps (each one graph launch); value from the median")
     ap.add_argument("--workload", default="llama3_8b_decode")
     ap.add_argument("--eager", action="store_true", help="launch forwards one by one instead of one HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--stream-calibration", action="store_true",
+                    help="measure the streaming-read ceiling over random chunks of 1-64 KB (attn_calib_stream_read)")
+    ap.add_argument("--summary-out", default=None, help="with --stream-calibration: write the text summary here")
     ap.add_argument("--kv-format", default="e4m3", choices=["e4m3", "int8"],
                     help="KV byte format of the attention workloads (INT8: two's complement times the page scale)")
     ap.add_argument("--json-out", default=None)
@@ -441,6 +563,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "reps": 5}))
+        return
+
+    if args.stream_calibration:
+        stream_calibration(dev, args)
         return
 
     from paged_fp8_kv_attn_amd import Plan, load_library
@@ -580,49 +706,72 @@ def main():
         graph.launch(stream)  # one untimed launch of the captured steps
         torch.cuda.synchronize()
 
-    # Timed region 1: the K steps (one graph launch, or eager launches).
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    if graph is not None:
-        graph.launch(stream)
-    else:
-        for i in range(args.steps):
-            fwd(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e1)
-    ms = total_ms / args.steps
+    # Timed region 1: R repetitions of the K steps (one graph launch each, or
+    # eager launches), each bracketed by a device synchronisation on both
+    # sides and timed with HIP events; the headline is the median repetition.
+    rep_ms = []
+    for _ in range(max(1, args.reps)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        if graph is not None:
+            graph.launch(stream)
+        else:
+            for i in range(args.steps):
+                fwd(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rep_ms.append(e0.elapsed_time(e1) / args.steps)
+    ms = float(np.median(rep_ms))
 
     # Timed region 2: the same K steps launched one by one, each attention
-    # kernel with a pair of HIP events that the library attaches to that
-    # kernel's own dispatch (they take its start and end timestamps).  A
-    # sleep kernel queued in front lets the host enqueue every step before
-    # the GPU reaches them, so the steps run back to back as in region 1.
+    # kernel (and merge kernel) with a pair of HIP events that the library
+    # attaches to that kernel's own dispatch (they take its start and end
+    # timestamps).  Replays of the captured graph queued in front keep the
+    # GPU busy, in the same state as in region 1, while the host enqueues
+    # every step, so the steps run back to back as in region 1 (eager mode:
+    # a sleep kernel does the same).
     hipt = HipGraph()
     ev = [([hipt.event() for _ in range(args.steps)], [hipt.event() for _ in range(args.steps)]) for _ in parts]
+    has_merge = [hasattr(pt.plan, "set_merge_events") for pt in parts]
+    mev = [([hipt.event() for _ in range(args.steps)], [hipt.event() for _ in range(args.steps)]) if hm else None
+           for hm in has_merge]
     torch.cuda.synchronize()
-    cal0 = torch.cuda.Event(enable_timing=True)
-    cal1 = torch.cuda.Event(enable_timing=True)
-    cal0.record(stream)
-    torch.cuda._sleep(1 << 20)
-    cal1.record(stream)
-    torch.cuda.synchronize()
-    sleep_ms_per_unit = cal0.elapsed_time(cal1) / (1 << 20)
     head_start_ms = 5.0 + 0.05 * args.steps * len(parts)  # generous: ~50 us of host time per forward
-    torch.cuda._sleep(int(head_start_ms / max(sleep_ms_per_unit, 1e-9)))
+    if graph is not None:
+        for _ in range(max(1, math.ceil(head_start_ms / max(ms * args.steps, 1e-6)))):
+            graph.launch(stream)
+    else:
+        cal0 = torch.cuda.Event(enable_timing=True)
+        cal1 = torch.cuda.Event(enable_timing=True)
+        cal0.record(stream)
+        torch.cuda._sleep(1 << 20)
+        cal1.record(stream)
+        torch.cuda.synchronize()
+        sleep_ms_per_unit = cal0.elapsed_time(cal1) / (1 << 20)
+        torch.cuda._sleep(int(head_start_ms / max(sleep_ms_per_unit, 1e-9)))
     for i in range(args.steps):
-        for pt, (starts, stops) in zip(parts, ev):
+        for pt, (starts, stops), me in zip(parts, ev, mev):
             pt.plan.set_kernel_events(starts[i], stops[i])
+            if me is not None:
+                pt.plan.set_merge_events(me[0][i], me[1][i])
             pt.forward(i, stream)
-    for pt in parts:
+    for pt, me in zip(parts, mev):
         pt.plan.set_kernel_events(None, None)
+        if me is not None:
+            pt.plan.set_merge_events(None, None)
     torch.cuda.synchronize()
-    for pt, (starts, stops) in zip(parts, ev):
+    # span of the eager, back-to-back steps: from the first attention kernel's
+    # start to the last step's last kernel end
+    eager_span_ms = hipt.elapsed_ms(ev[0][0][0], ev[-1][1][-1]) if mev[-1] is None else \
+        hipt.elapsed_ms(ev[0][0][0], mev[-1][1][-1])
+    eager_step_ms = eager_span_ms / args.steps
+    for pt, (starts, stops), me in zip(parts, ev, mev):
         pt.kernel_ms = [hipt.elapsed_ms(a, b) for a, b in zip(starts, stops)]
         pt.attn_ms = float(np.mean(pt.kernel_ms))
-        for e in starts + stops:
+        pt.merge_ms = [hipt.elapsed_ms(a, b) for a, b in zip(*me)] if me is not None else []
+        for e in starts + stops + (me[0] + me[1] if me is not None else []):
             hipt.destroy_event(e)
 
     def roofline(pt, traffic):
@@ -635,6 +784,16 @@ def main():
         else:
             roof = {"bound": "hbm", "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": k_gbs / HBM_PEAK_GBS, "traffic": traffic}
+        if roof["bound"] == "hbm":
+            ceil = committed_stream_ceiling(pt.w)
+            if ceil is not None:
+                roof["stream_ceiling"] = {"GB/s": ceil["GB/s"], "chunk_bytes": ceil["chunk_bytes"],
+                                          "frac": k_gbs / ceil["GB/s"], "source": ceil["source"]}
+        sq = committed_sq_counters(profile_name(pt.w), pt.kernel)
+        if sq is not None:
+            roof["sq_counters"] = sq
+        if pt.merge_ms:
+            roof["merge_avg_us"] = float(np.mean(pt.merge_ms)) * 1e3
         roof.update({"kernel": pt.kernel, "kernel_avg_us": pt.attn_ms * 1e3,
                      "kernel_median_us": float(np.median(pt.kernel_ms)) * 1e3,
                      "kernel_min_us": float(np.min(pt.kernel_ms)) * 1e3,
@@ -676,6 +835,10 @@ def main():
         "data": "synthetic",
         "config": config,
         "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "reps": len(rep_ms),
+        "rep_ms_per_step": rep_ms,
+        "rep_spread": (max(rep_ms) - min(rep_ms)) / ms if ms > 0 else None,
+        "eager_ms_per_step": eager_step_ms,
         "query_tokens_per_s": qtok,
         "tflops": tflops,
         "launch": "graph" if graph is not None else "eager",

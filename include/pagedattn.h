@@ -186,6 +186,12 @@ attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info);
 attn_status_t attn_plan_set_kernel_events(attn_plan_t plan, hipEvent_t attention_start,
                                           hipEvent_t attention_stop);
 
+/* Measurement hook, as attn_plan_set_kernel_events for the log-sum-exp merge
+ * kernel a forward launches after the attention kernel when keys were split.
+ * A forward that launches no merge records both events at the same point of
+ * the stream (zero duration). */
+attn_status_t attn_plan_set_merge_events(attn_plan_t plan, hipEvent_t merge_start, hipEvent_t merge_stop);
+
 /* ---- the step before the attention: appending new tokens' K/V ----------
  * Follows the same passages as the attention (memory section: fixed-size
  * blocks of a preallocated pool; quantisation section: FP8 with per-group
@@ -285,6 +291,28 @@ attn_status_t attn_debug_decode_int8(const uint8_t* in, float* out, int64_t n, h
  * (nearest code, ties to even, magnitudes above 448 saturated, sign kept;
  * finite inputs).  n >= 0; n == 0 enqueues nothing. */
 attn_status_t attn_debug_encode_fp8(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+/* ---- measurement hook: the streaming-read ceiling ----
+ * The HBM fraction of the attention kernels is reported against the MI355X
+ * peak and against what this kernel reaches for the same access pattern: it
+ * reads num_chunks chunks of chunk_bytes contiguous bytes, chunk i starting at
+ * pool + chunk_ids[i] * chunk_bytes (a paged KV cache reads every (page, kv
+ * head) as one such chunk, at a random place of the pool), with 16-byte
+ * loads, `waves` waves each streaming an equal contiguous share of the list,
+ * and writes one XOR word per lane to sink (waves * 64 uint32, so the loads
+ * cannot be dropped).  No other arithmetic.
+ *   pool        device memory of pool_bytes (>= chunk_bytes), 16-byte aligned;
+ *               ids outside [0, pool_bytes / chunk_bytes) are clamped into it
+ *   chunk_ids   int32 [num_chunks], device memory
+ *   chunk_bytes a power of two in [1024, 2^24]
+ *   waves       1 .. 2^20
+ *   kernel_start, kernel_stop  when both non-null, attached to the kernel's
+ *               own dispatch (its duration alone); null otherwise.
+ * Asynchronous on `stream`; allocates nothing.  Not part of the attention
+ * path. */
+attn_status_t attn_calib_stream_read(const uint8_t* pool, int64_t pool_bytes, const int32_t* chunk_ids,
+                                     int64_t num_chunks, int32_t chunk_bytes, int32_t waves, uint32_t* sink,
+                                     hipEvent_t kernel_start, hipEvent_t kernel_stop, hipStream_t stream);
 
 #ifdef __cplusplus
 }

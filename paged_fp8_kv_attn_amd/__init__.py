@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     Plan,
     PlanInfo,
+    calib_stream_read,
     debug_decode_fp8,
     debug_decode_int8,
     debug_encode_fp8,
@@ -16,6 +17,7 @@ from ._binding import (  # noqa: F401
     exported_symbols,
     library_path,
     load_library,
+    make_desc,
     mtp_accept,
     mtp_accept_workspace_size,
     status_string,

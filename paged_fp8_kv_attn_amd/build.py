@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["attn_abi.hip", "attn_stream.hip", "attn_debug.hip", "attn_append.hip", "attn_accept.hip"]
+SOURCES = ["attn_abi.hip", "attn_stream.hip", "attn_debug.hip", "attn_append.hip", "attn_accept.hip", "attn_calib.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -37,6 +37,7 @@ struct attn_plan_s {
   float sm_scale;
   void* workspace;
   size_t workspace_bytes;
+  size_t ws_o_bytes, ws_ml_bytes, ws_r0_bytes;  // byte sizes of the workspace's parts
   float* part_o;
   float* part_ml;
   int32_t* seq_row0;
@@ -45,6 +46,8 @@ struct attn_plan_s {
   int merge_cols;  // query columns per merge workgroup
   hipEvent_t ev_start;  // optional: recorded around the attention kernel
   hipEvent_t ev_stop;
+  hipEvent_t mev_start;  // optional: recorded around the merge kernel
+  hipEvent_t mev_stop;
 };
 
 namespace {
@@ -59,6 +62,8 @@ attn_status_t hip_fail(hipError_t e) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+size_t round_up256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 constexpr int kChunkTokens = 32;  // keys per chunk (two pages)
 constexpr int kMinChunksPerGroup = 16;  // a workgroup's share is at least 4 chunks per wave
@@ -95,33 +100,12 @@ attn_status_t validate_desc(const attn_plan_desc_t& d) {
   return ATTN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* attn_status_string(attn_status_t s) {
-  switch (s) {
-    case ATTN_OK: return "ATTN_OK: success";
-    case ATTN_ERR_INVALID_ARGUMENT: return "ATTN_ERR_INVALID_ARGUMENT: null/misaligned pointer or inconsistent descriptor";
-    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: request outside what this library implements";
-    case ATTN_ERR_OUT_OF_MEMORY: return "ATTN_ERR_OUT_OF_MEMORY: workspace allocation failed";
-    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: a HIP runtime call failed (see attn_last_hip_error)";
-  }
-  return "unknown attn_status_t";
-}
-
-int attn_last_hip_error(void) { return g_last_hip_error; }
-
-attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_plan) {
-  if (!desc || !out_plan) return ATTN_ERR_INVALID_ARGUMENT;
-  *out_plan = nullptr;
-  const attn_status_t st = validate_desc(*desc);
-  if (st != ATTN_OK) return st;
-  const attn_plan_desc_t& d = *desc;
-
-  attn_plan_s* p = new (std::nothrow) attn_plan_s();
-  if (!p) return ATTN_ERR_OUT_OF_MEMORY;
+// The plan's choices for desc on `device` -- column tiles, kernel variant,
+// units, grid, merge shape and the workspace size -- with no allocation and
+// no device work; p->workspace and the pointers into it stay null.
+attn_status_t choose_plan(const attn_plan_desc_t& d, int device, attn_plan_s* p) {
   p->desc = d;
+  p->device = device;
   p->group = d.num_q_heads / d.num_kv_heads;
   p->sm_scale = d.sm_scale > 0.f ? d.sm_scale : 1.0f / std::sqrt(static_cast<float>(d.head_dim));
 
@@ -168,7 +152,6 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   p->col_blocks = ceil_div(cols, p->cols_per_block);
   p->variant = v;
 
-  p->num_segments = 0;
   p->workspace = nullptr;
   p->workspace_bytes = 0;
   p->part_o = nullptr;
@@ -177,26 +160,17 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   p->seg_merge = nullptr;
   p->ev_start = nullptr;
   p->ev_stop = nullptr;
+  p->mev_start = nullptr;
+  p->mev_stop = nullptr;
   const int64_t segments = static_cast<int64_t>(d.num_seqs) * d.num_kv_heads * p->col_blocks;
-  if (segments > 0x3fffffffLL) {
-    delete p;
-    return ATTN_ERR_UNSUPPORTED;
-  }
+  if (segments > 0x3fffffffLL || segments * p->cols_per_block > 0x3fffffffLL) return ATTN_ERR_UNSUPPORTED;
   p->num_segments = static_cast<int>(segments);
-  if (segments * p->cols_per_block > 0x3fffffffLL) {
-    delete p;
-    return ATTN_ERR_UNSUPPORTED;
-  }
 
-  if (hipGetDevice(&p->device) != hipSuccess) {
-    delete p;
-    return hip_fail(hipGetLastError());
-  }
   // Workgroups of the attention kernel: by default as many as the GPU keeps
   // resident at once (every one then streams an equal share of the chunks in
   // a single round), and no more than one per kMinChunksPerGroup chunks of
   // the largest lengths, so that small problems are not split at all.
-  hipError_t e = hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device);
+  hipError_t e = hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e == hipSuccess) e = pa::stream_attention_occupancy(v, &p->occupancy);
   if (e == hipSuccess && v.packed && d.num_kv_splits > 0) {
     // Packed decode with two groups in flight holds one wave per SIMD; when a
@@ -210,10 +184,7 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
       e = pa::stream_attention_occupancy(v, &p->occupancy);
     }
   }
-  if (e != hipSuccess) {
-    delete p;
-    return hip_fail(e);
-  }
+  if (e != hipSuccess) return hip_fail(e);
   if (p->occupancy < 1) p->occupancy = 1;
   // Units sharing the chunks: waves for the packed decode layout (each wave
   // streams its own range), workgroups otherwise.  By default as many as
@@ -234,10 +205,7 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   }
   units = std::min<int64_t>(units, std::max<int64_t>(1, max_chunks / p->unit_min_chunks));
   units = std::max<int64_t>(units, 1);
-  if (units > 0x3fffffffLL) {
-    delete p;
-    return ATTN_ERR_UNSUPPORTED;
-  }
+  if (units > 0x3fffffffLL) return ATTN_ERR_UNSUPPORTED;
   p->max_units = static_cast<int>(units);
   // A unit that begins a segment inside its range restarts its load
   // pipeline (block-table batch, then the first KV chunks; in the tile
@@ -255,30 +223,129 @@ attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_pl
   p->merge_grid = units > 1 ? p->num_segments : 0;
   p->merge_cols = pa::merge_cols_for(v, p->cols_per_block, (units + segments - 1) / segments);
 
-  // Workspace, allocated once: partial slots (segments + units of them, one
-  // per (segment, unit) pair that can occur), each sequence's first query
-  // row, and each segment's partial slots.
+  // Workspace: partial slots (segments + units of them, one per (segment,
+  // unit) pair that can occur), each sequence's first query row, and each
+  // segment's partial slots.
   const size_t slots = static_cast<size_t>(segments) + static_cast<size_t>(units);
-  const size_t o_bytes = slots * p->cols_per_block * d.head_dim * sizeof(float);
-  const size_t ml_bytes = slots * p->cols_per_block * 2 * sizeof(float);
-  const size_t r0_bytes = static_cast<size_t>(d.num_seqs) * sizeof(int32_t);
-  const size_t job_bytes = static_cast<size_t>(segments) * 2 * sizeof(int32_t);
-  auto round_up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  p->workspace_bytes = round_up(o_bytes) + round_up(ml_bytes) + round_up(r0_bytes) + round_up(job_bytes);
-  e = hipMalloc(&p->workspace, p->workspace_bytes);
+  p->ws_o_bytes = round_up256(slots * p->cols_per_block * d.head_dim * sizeof(float));
+  p->ws_ml_bytes = round_up256(slots * p->cols_per_block * 2 * sizeof(float));
+  p->ws_r0_bytes = round_up256(static_cast<size_t>(d.num_seqs) * sizeof(int32_t));
+  const size_t job_bytes = round_up256(static_cast<size_t>(segments) * 2 * sizeof(int32_t));
+  p->workspace_bytes = p->ws_o_bytes + p->ws_ml_bytes + p->ws_r0_bytes + job_bytes;
+  return ATTN_OK;
+}
+
+// Point the plan's partial buffers into `base` (workspace_bytes of device
+// memory, 256-byte aligned).
+void place_workspace(attn_plan_s* p, void* base) {
+  char* ws = static_cast<char*>(base);
+  p->workspace = base;
+  p->part_o = reinterpret_cast<float*>(ws);
+  ws += p->ws_o_bytes;
+  p->part_ml = reinterpret_cast<float*>(ws);
+  ws += p->ws_ml_bytes;
+  p->seq_row0 = reinterpret_cast<int32_t*>(ws);
+  ws += p->ws_r0_bytes;
+  p->seg_merge = reinterpret_cast<int2*>(ws);
+}
+
+attn_status_t check_forward_args(const void* q, const uint8_t* k_pages, const uint8_t* v_pages,
+                                 const float* kv_scales, const int32_t* block_table, const int32_t* ctx_lens,
+                                 const int32_t* q_lens, const void* out) {
+  if (!q || !k_pages || !v_pages || !kv_scales || !block_table || !ctx_lens || !q_lens || !out)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16) ||
+      !aligned(kv_scales, 4) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) || !aligned(q_lens, 4))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  return ATTN_OK;
+}
+
+// Enqueue the attention kernel, and the merge kernel when keys were split,
+// of a plan whose workspace pointers are placed.
+attn_status_t enqueue_forward(const attn_plan_s* plan, const void* q, const uint8_t* k_pages,
+                              const uint8_t* v_pages, const float* kv_scales, const int32_t* block_table,
+                              const int32_t* ctx_lens, const int32_t* q_lens, void* out, hipStream_t stream) {
+  const attn_plan_desc_t& d = plan->desc;
+  pa::StreamParams sp{};
+  sp.q = q;
+  sp.k_pages = k_pages;
+  sp.v_pages = v_pages;
+  sp.kv_scales = kv_scales;
+  sp.block_table = block_table;
+  sp.ctx_lens = ctx_lens;
+  sp.q_lens = q_lens;
+  sp.out = out;
+  sp.part_o = plan->part_o;
+  sp.part_ml = plan->part_ml;
+  sp.num_seqs = d.num_seqs;
+  sp.num_q_heads = d.num_q_heads;
+  sp.num_kv_heads = d.num_kv_heads;
+  sp.group = plan->group;
+  sp.bt_stride = d.max_pages_per_seq;
+  sp.max_q_len = d.max_q_len;
+  sp.cols_per_block = plan->cols_per_block;
+  sp.col_blocks = plan->col_blocks;
+  sp.merge_cols = plan->merge_cols;
+  sp.unit_min_chunks = plan->unit_min_chunks;
+  sp.max_units = plan->max_units;
+  sp.start_cost = plan->start_cost;
+  sp.seq_row0 = plan->seq_row0;
+  sp.seg_merge = plan->seg_merge;
+  sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
+  sp.qk_scale_log2 = plan->sm_scale * 1.4426950408889634f;
+
+  hipError_t e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream, plan->ev_start, plan->ev_stop);
+  if (e == hipSuccess && plan->merge_grid > 0) {
+    e = pa::launch_split_merge(plan->variant, sp, plan->merge_grid, stream, plan->mev_start, plan->mev_stop);
+  } else if (e == hipSuccess && plan->mev_start) {
+    // no merge launched: both events mark the same point of the stream
+    e = hipEventRecord(plan->mev_start, stream);
+    if (e == hipSuccess) e = hipEventRecord(plan->mev_stop, stream);
+  }
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK: success";
+    case ATTN_ERR_INVALID_ARGUMENT: return "ATTN_ERR_INVALID_ARGUMENT: null/misaligned pointer or inconsistent descriptor";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: request outside what this library implements";
+    case ATTN_ERR_OUT_OF_MEMORY: return "ATTN_ERR_OUT_OF_MEMORY: workspace allocation failed";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: a HIP runtime call failed (see attn_last_hip_error)";
+  }
+  return "unknown attn_status_t";
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+attn_status_t attn_plan_create(const attn_plan_desc_t* desc, attn_plan_t* out_plan) {
+  if (!desc || !out_plan) return ATTN_ERR_INVALID_ARGUMENT;
+  *out_plan = nullptr;
+  const attn_status_t st = validate_desc(*desc);
+  if (st != ATTN_OK) return st;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return hip_fail(hipGetLastError());
+
+  attn_plan_s* p = new (std::nothrow) attn_plan_s();
+  if (!p) return ATTN_ERR_OUT_OF_MEMORY;
+  const attn_status_t cs = choose_plan(*desc, device, p);
+  if (cs != ATTN_OK) {
+    delete p;
+    return cs;
+  }
+  // the workspace, allocated once
+  void* ws = nullptr;
+  const hipError_t e = hipMalloc(&ws, p->workspace_bytes);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     delete p;
     return e == hipErrorOutOfMemory ? ATTN_ERR_OUT_OF_MEMORY : hip_fail(e);
   }
-  char* ws = static_cast<char*>(p->workspace);
-  p->part_o = reinterpret_cast<float*>(ws);
-  ws += round_up(o_bytes);
-  p->part_ml = reinterpret_cast<float*>(ws);
-  ws += round_up(ml_bytes);
-  p->seq_row0 = reinterpret_cast<int32_t*>(ws);
-  ws += round_up(r0_bytes);
-  p->seg_merge = reinterpret_cast<int2*>(ws);
+  place_workspace(p, ws);
   *out_plan = p;
   return ATTN_OK;
 }
@@ -321,6 +388,14 @@ attn_status_t attn_plan_set_kernel_events(attn_plan_t plan, hipEvent_t attention
   return ATTN_OK;
 }
 
+attn_status_t attn_plan_set_merge_events(attn_plan_t plan, hipEvent_t merge_start, hipEvent_t merge_stop) {
+  if (!plan) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((merge_start == nullptr) != (merge_stop == nullptr)) return ATTN_ERR_INVALID_ARGUMENT;
+  plan->mev_start = merge_start;
+  plan->mev_stop = merge_stop;
+  return ATTN_OK;
+}
+
 static attn_status_t check_device(const attn_plan_s* plan) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return hip_fail(hipGetLastError());
@@ -330,47 +405,12 @@ static attn_status_t check_device(const attn_plan_s* plan) {
 attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t* k_pages, const uint8_t* v_pages,
                                  const float* kv_scales, const int32_t* block_table, const int32_t* ctx_lens,
                                  const int32_t* q_lens, void* out, hipStream_t stream) {
-  if (!plan || !q || !k_pages || !v_pages || !kv_scales || !block_table || !ctx_lens || !q_lens || !out)
-    return ATTN_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16) ||
-      !aligned(kv_scales, 4) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) || !aligned(q_lens, 4))
-    return ATTN_ERR_INVALID_ARGUMENT;
+  if (!plan) return ATTN_ERR_INVALID_ARGUMENT;
+  const attn_status_t ast = check_forward_args(q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out);
+  if (ast != ATTN_OK) return ast;
   const attn_status_t dst = check_device(plan);
   if (dst != ATTN_OK) return dst;
-
-  const attn_plan_desc_t& d = plan->desc;
-  pa::StreamParams sp{};
-  sp.q = q;
-  sp.k_pages = k_pages;
-  sp.v_pages = v_pages;
-  sp.kv_scales = kv_scales;
-  sp.block_table = block_table;
-  sp.ctx_lens = ctx_lens;
-  sp.q_lens = q_lens;
-  sp.out = out;
-  sp.part_o = plan->part_o;
-  sp.part_ml = plan->part_ml;
-  sp.num_seqs = d.num_seqs;
-  sp.num_q_heads = d.num_q_heads;
-  sp.num_kv_heads = d.num_kv_heads;
-  sp.group = plan->group;
-  sp.bt_stride = d.max_pages_per_seq;
-  sp.max_q_len = d.max_q_len;
-  sp.cols_per_block = plan->cols_per_block;
-  sp.col_blocks = plan->col_blocks;
-  sp.merge_cols = plan->merge_cols;
-  sp.unit_min_chunks = plan->unit_min_chunks;
-  sp.max_units = plan->max_units;
-  sp.start_cost = plan->start_cost;
-  sp.seq_row0 = plan->seq_row0;
-  sp.seg_merge = plan->seg_merge;
-  sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
-  sp.qk_scale_log2 = plan->sm_scale * 1.4426950408889634f;
-
-  hipError_t e = pa::launch_stream_attention(plan->variant, sp, plan->grid, stream, plan->ev_start, plan->ev_stop);
-  if (e == hipSuccess && plan->merge_grid > 0)
-    e = pa::launch_split_merge(plan->variant, sp, plan->merge_grid, stream);
-  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+  return enqueue_forward(plan, q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out, stream);
 }
 
 attn_status_t attn_debug_gather(attn_plan_t plan, const uint8_t* k_pages, const uint8_t* v_pages,
@@ -470,6 +510,22 @@ attn_status_t attn_mtp_accept(const void* logits, attn_dtype_t logits_dtype, con
   ap.vocab = vocab;
   ap.segments = pa::accept_segments(rows, vocab);
   const hipError_t e = pa::launch_mtp_accept(ap, logits_dtype == ATTN_DTYPE_F32, stream, kernel_start, kernel_stop);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+attn_status_t attn_calib_stream_read(const uint8_t* pool, int64_t pool_bytes, const int32_t* chunk_ids,
+                                     int64_t num_chunks, int32_t chunk_bytes, int32_t waves, uint32_t* sink,
+                                     hipEvent_t kernel_start, hipEvent_t kernel_stop, hipStream_t stream) {
+  if (!pool || !chunk_ids || !sink) return ATTN_ERR_INVALID_ARGUMENT;
+  if (chunk_bytes < 1024 || chunk_bytes > (1 << 24) || (chunk_bytes & (chunk_bytes - 1)) != 0)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (pool_bytes < chunk_bytes || num_chunks < 1 || num_chunks > (int64_t{1} << 40) / chunk_bytes)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (waves < 1 || waves > (1 << 20)) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((kernel_start == nullptr) != (kernel_stop == nullptr)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(pool, 16) || !aligned(chunk_ids, 4) || !aligned(sink, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  const hipError_t e = pa::launch_stream_read(pool, pool_bytes, chunk_ids, num_chunks, chunk_bytes, waves, sink,
+                                              stream, kernel_start, kernel_stop);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

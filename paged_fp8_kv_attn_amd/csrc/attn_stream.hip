@@ -1721,20 +1721,24 @@ int merge_grid_y(int cols_per_block, int merge_cols) {
   return (cols_per_block + merge_cols - 1) / merge_cols;
 }
 
-hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream) {
+hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream,
+                              hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (grid <= 0) return hipSuccess;
   const dim3 g(grid, merge_grid_y(p.cols_per_block, p.merge_cols));
   const dim3 block(kMergeThreads);
+  const void* f = nullptr;
   if (v.head_dim == 128) {
-    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<128, true>), g, block, 0, stream, p);
-    else hipLaunchKernelGGL((split_merge_kernel<128, false>), g, block, 0, stream, p);
+    f = v.out_f32 ? reinterpret_cast<const void*>(&split_merge_kernel<128, true>)
+                  : reinterpret_cast<const void*>(&split_merge_kernel<128, false>);
   } else if (v.head_dim == 64) {
-    if (v.out_f32) hipLaunchKernelGGL((split_merge_kernel<64, true>), g, block, 0, stream, p);
-    else hipLaunchKernelGGL((split_merge_kernel<64, false>), g, block, 0, stream, p);
+    f = v.out_f32 ? reinterpret_cast<const void*>(&split_merge_kernel<64, true>)
+                  : reinterpret_cast<const void*>(&split_merge_kernel<64, false>);
   } else {
     return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  void* args[] = {const_cast<StreamParams*>(&p)};
+  if (ev_start) return hipExtLaunchKernel(f, g, block, args, 0, stream, ev_start, ev_stop, 0);
+  return hipLaunchKernel(f, g, block, args, 0, stream);
 }
 
 }  // namespace pa

@@ -11,8 +11,8 @@ constexpr int kPageSize = 16;  // tokens per page
 
 struct StreamParams {
   const void* q;               // [sum Q][Hq][D] bf16 or fp32
-  const uint8_t* k_pages;      // [P][Hkv][16][D]
-  const uint8_t* v_pages;      // [P][Hkv][4][D][4]
+  const uint8_t* k_pages;      // [P][Hkv][D/16][16][16]
+  const uint8_t* v_pages;      // [P][Hkv][4][D/64][16][4][4]
   const float* kv_scales;      // [2][P][Hkv]
   const int32_t* block_table;  // [B][bt_stride]
   const int32_t* ctx_lens;     // [B]
@@ -72,7 +72,8 @@ hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int 
 // Resident workgroups per compute unit for the variant's attention kernel.
 hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu);
 // Merge kernel: `grid` = segments workgroups along x, merge_grid_y along y.
-hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream);
+hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream,
+                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 int merge_cols_for(const Variant& v, int cols_per_block, int64_t expected_parts);
 int merge_grid_y(int cols_per_block, int merge_cols);
 
@@ -134,6 +135,12 @@ hipError_t launch_mtp_accept(const AcceptParams& p, bool f32, hipStream_t stream
                              hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_debug_gather(const GatherParams& p, hipStream_t stream);
+// Streaming-read calibration: `waves` waves read the chunk_bytes-sized chunks
+// ids[0..num_chunks) of pool (ids clamped to the pool) and write one XOR word
+// per lane to sink[waves * 64].  chunk_bytes: a power of two >= 1024.
+hipError_t launch_stream_read(const uint8_t* pool, int64_t pool_bytes, const int32_t* ids, int64_t num_chunks,
+                              int32_t chunk_bytes, int32_t waves, uint32_t* sink, hipStream_t stream,
+                              hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, bool kv_int8, hipStream_t stream);
 
 }  // namespace pa
