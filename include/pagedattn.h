@@ -192,6 +192,33 @@ attn_status_t attn_plan_set_kernel_events(attn_plan_t plan, hipEvent_t attention
  * the stream (zero duration). */
 attn_status_t attn_plan_set_merge_events(attn_plan_t plan, hipEvent_t merge_start, hipEvent_t merge_stop);
 
+/* ---- allocation-free forward ----
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture that must not call hipMalloc, tight serving loops, harnesses that
+ * forbid allocation.  It computes exactly what attn_paged_forward computes
+ * for a plan made from *desc (the same choices, kernels and result), but
+ * takes the descriptor instead of a plan and keeps the split partials in a
+ * library-owned device array of attn_static_scratch_bytes() bytes (32 MiB),
+ * one per GPU, held until the process ends; it calls no hipMalloc or
+ * hipFree.  The array's device address is looked up on the first call on
+ * each device.
+ *   desc, q .. out, stream: as attn_plan_create and attn_paged_forward (the
+ *   current device is the one used).
+ * Errors: as those two; ATTN_ERR_UNSUPPORTED when the workspace a plan for
+ * *desc needs (attn_plan_info_t.workspace_bytes) exceeds the array, e.g. the
+ * 8 x 512-token prefill chunk of 32 query / 8 kv heads (~100 MB).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, or two host threads) race and give wrong
+ * results; calls on one stream are ordered and safe.  Nothing in the array
+ * needs to start at zero (each forward writes what it reads). */
+attn_status_t attn_paged_forward_static(const attn_plan_desc_t* desc, const void* q, const uint8_t* k_pages,
+                                        const uint8_t* v_pages, const float* kv_scales, const int32_t* block_table,
+                                        const int32_t* ctx_lens, const int32_t* q_lens, void* out,
+                                        hipStream_t stream);
+
+/* Size in bytes of the per-GPU array attn_paged_forward_static uses. */
+size_t attn_static_scratch_bytes(void);
+
 /* ---- the step before the attention: appending new tokens' K/V ----------
  * Follows the same passages as the attention (memory section: fixed-size
  * blocks of a preallocated pool; quantisation section: FP8 with per-group

@@ -15,10 +15,12 @@ from ._binding import (  # noqa: F401
     debug_encode_fp8,
     debug_gather,
     exported_symbols,
+    forward_static,
     library_path,
     load_library,
     make_desc,
     mtp_accept,
     mtp_accept_workspace_size,
+    static_scratch_bytes,
     status_string,
 )

@@ -36,6 +36,8 @@ _FUNCTIONS = [
     "attn_mtp_accept_workspace_size",
     "attn_mtp_accept",
     "attn_calib_stream_read",
+    "attn_paged_forward_static",
+    "attn_static_scratch_bytes",
 ]
 
 
@@ -139,6 +141,10 @@ def load_library():
     lib.attn_mtp_accept.restype = i32
     lib.attn_calib_stream_read.argtypes = [vp, i64, vp, i64, i32, i32, vp, vp, vp, vp]
     lib.attn_calib_stream_read.restype = i32
+    lib.attn_paged_forward_static.argtypes = [ctypes.POINTER(PlanDesc)] + [vp] * 9
+    lib.attn_paged_forward_static.restype = i32
+    lib.attn_static_scratch_bytes.argtypes = []
+    lib.attn_static_scratch_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -277,6 +283,23 @@ def make_desc(*, num_seqs, num_q_heads, num_kv_heads, head_dim, num_pages, max_p
     for i, r in enumerate(reserved):
         d.reserved[i] = r
     return d
+
+
+def forward_static(desc: PlanDesc, q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out,
+                   stream=None):
+    """attn_paged_forward_static: the forward of a plan for `desc`, with the
+    split partials in the library's per-GPU scratch array (no allocation)."""
+    _want(q, "q", None, (torch.bfloat16, torch.float32))
+    check_forward_tensors(desc, q.device, q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out)
+    st = load_library().attn_paged_forward_static(
+        ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(kv_scales), _ptr(block_table),
+        _ptr(ctx_lens), _ptr(q_lens), _ptr(out), _stream(stream))
+    _check(st, "attn_paged_forward_static")
+    return out
+
+
+def static_scratch_bytes() -> int:
+    return int(load_library().attn_static_scratch_bytes())
 
 
 class Plan:

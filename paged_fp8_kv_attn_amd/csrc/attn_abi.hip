@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/pagedattn.h"
@@ -305,6 +306,33 @@ attn_status_t enqueue_forward(const attn_plan_s* plan, const void* q, const uint
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+// ---- the allocation-free forward's scratch ---------------------------------
+// Device memory that attn_paged_forward_static uses in place of a plan's
+// workspace: one file-scope array per GPU, held until the process ends.  In
+// host code the array's name is only a stand-in for the symbol: its device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is passed to kernels.
+constexpr size_t kStaticScratchBytes = size_t{32} << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on `device` (current), looked up on the first call.
+attn_status_t static_scratch(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !a) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    g_scratch_ptr[device] = a;
+  }
+  *ptr = g_scratch_ptr[device];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,6 +440,31 @@ attn_status_t attn_paged_forward(attn_plan_t plan, const void* q, const uint8_t*
   if (dst != ATTN_OK) return dst;
   return enqueue_forward(plan, q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out, stream);
 }
+
+attn_status_t attn_paged_forward_static(const attn_plan_desc_t* desc, const void* q, const uint8_t* k_pages,
+                                        const uint8_t* v_pages, const float* kv_scales, const int32_t* block_table,
+                                        const int32_t* ctx_lens, const int32_t* q_lens, void* out,
+                                        hipStream_t stream) {
+  if (!desc) return ATTN_ERR_INVALID_ARGUMENT;
+  const attn_status_t vst = validate_desc(*desc);
+  if (vst != ATTN_OK) return vst;
+  const attn_status_t ast = check_forward_args(q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out);
+  if (ast != ATTN_OK) return ast;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return hip_fail(hipGetLastError());
+  void* ws = nullptr;
+  const attn_status_t sst = static_scratch(device, &ws);
+  if (sst != ATTN_OK) return sst;
+  // the same choices as attn_plan_create, in a plan on the stack
+  attn_plan_s plan;
+  const attn_status_t cst = choose_plan(*desc, device, &plan);
+  if (cst != ATTN_OK) return cst;
+  if (plan.workspace_bytes > kStaticScratchBytes) return ATTN_ERR_UNSUPPORTED;
+  place_workspace(&plan, ws);
+  return enqueue_forward(&plan, q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out, stream);
+}
+
+size_t attn_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
 attn_status_t attn_debug_gather(attn_plan_t plan, const uint8_t* k_pages, const uint8_t* v_pages,
                                 const float* kv_scales, const int32_t* block_table, const int32_t* ctx_lens,
