@@ -53,6 +53,17 @@
 #include "device_common.h"
 #include "kernel_params.h"
 
+// Eight-wave workgroups (two waves per SIMD from one workgroup, meeting at
+// the same barrier every chunk) run the ping-pong schedule.
+#ifndef TILE_PINGPONG
+#define TILE_PINGPONG 1
+#endif
+// Which waves lead: the first half (waves w and w + 4 share a SIMD when the
+// dispatcher places wave w on SIMD w % 4), or the even ones.
+#ifndef TILE_PP_PARITY
+#define TILE_PP_PARITY 0
+#endif
+
 namespace pa {
 
 namespace {
@@ -1099,7 +1110,7 @@ __device__ __forceinline__ void load_q_operand(const StreamParams& p, size_t qof
   }
 }
 
-template <int D, int NW, int NT, bool QF32, bool OUTF32, int R, bool KI8>
+template <int D, int NW, int NT, bool QF32, bool OUTF32, int R, bool KI8, bool PP>
 __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const PieceDesc& pc, int lane, int wave) {
   using GD = Geo<D>;
   using TG = TileGeo<D, NW>;
@@ -1135,11 +1146,12 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
   }
 
   f32x4 o[NT][GD::NVB];
-  float m[NT], l[NT];
+  float m[NT], l[NT], base[NT];  // base: the exponent reference, m or 0 while m = -inf
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     m[t] = kNegInf;
     l[t] = 0.f;
+    base[t] = 0.f;
 #pragma unroll
     for (int c = 0; c < GD::NVB; ++c) o[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -1164,21 +1176,26 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
     }
   }
 
-  __shared__ bf16x8 s_kv[2][TG::SLOTS][64];
-  // the previous piece may still read either buffer
+  // Converted chunks in LDS: two buffers, or three with the ping-pong
+  // schedule (the lagging half of the waves still reads chunk k - 1 after
+  // the barrier that publishes chunk k).
+  constexpr int NB = PP ? 3 : 2;
+  __shared__ bf16x8 s_kv[NB][TG::SLOTS][64];
+  // the previous piece may still read any buffer
   lds_barrier();
 
   const int32_t* bt = p.block_table + (size_t)pc.b * p.bt_stride;
   const int c_begin = pc.c_begin;
   const int nk = pc.c_end - c_begin;
   // block-table batch: lane j holds the page of chunk k0 + j/2, position j%2,
-  // with that page's K and V scales
+  // with that page's score factor (K scale times sm_scale log2 e) and log2
+  // of its V scale
   int32_t bt_v = 0;
-  float sk_v = 0.f, sv_v = 0.f;
+  float sk_v = 0.f, lv_v = 0.f;
   auto load_batch = [&](int k0) {
     const int k = k0 + (lane >> 1);
     int32_t ph = 0;
-    float a = 0.f, bsc = 0.f;
+    float a = 0.f, bsc = 1.f;
     if (k < nk) {
       const int pg = min(2 * (c_begin + k) + (lane & 1), npages - 1);  // a missing second page repeats the first
       ph = bt[pg];
@@ -1187,13 +1204,18 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
       bsc = p.kv_scales[p.v_scale_offset + sidx];
     }
     bt_v = ph;
-    sk_v = a;
-    sv_v = bsc;
-    settle_batch(bt_v, sk_v, sv_v);
+    sk_v = a * p.qk_scale_log2;
+    lv_v = __builtin_log2f(bsc);
+    settle_batch(bt_v, sk_v, lv_v);
   };
 
+  // what the softmax of a chunk needs: per page, the score factor and log2
+  // of the V scale
+  struct ChunkMeta {
+    float fk[2], lv[2];
+  };
   u32x4 raw[R][TG::LPT];
-  float skr[R][2], svr[R][2];
+  ChunkMeta rm[R];
   auto issue = [&](int k, int j) {
     if ((k & 31) == 0) load_batch(k);
     const int e = 2 * (k & 31);
@@ -1206,17 +1228,17 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
     }
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
-      skr[j][pg] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sk_v), e + pg));
-      svr[j][pg] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sv_v), e + pg));
+      rm[j].fk[pg] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sk_v), e + pg));
+      rm[j].lv[pg] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lv_v), e + pg));
     }
   };
 
-  // scales of the chunk between its consume and compute (its ring buffer is
-  // refilled in between)
-  float csk[2], csv[2];
+  // the chunk between its consume and compute (its ring buffer is refilled
+  // in between)
+  ChunkMeta cm;
   auto consume = [&](int k, int j) {
     const int c = c_begin + k;
-    bf16x8 (*dst)[64] = s_kv[k & 1];
+    bf16x8 (*dst)[64] = s_kv[k % NB];
 #pragma unroll
     for (int r = 0; r < TG::LPT; ++r) {
       const u32x4 w = raw[j][r];
@@ -1240,19 +1262,12 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
           reinterpret_cast<bf16x4*>(&dst[TG::KSL + 4 * i + e][lane])[ldpg[r]] = kv8x4_to_bf16x4<KI8>(w[e] & vm);
       }
     }
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      csk[pg] = skr[j][pg];
-      csv[pg] = svr[j][pg];
-    }
+    cm = rm[j];
   };
 
-  auto compute = [&](int k) {
-    lds_barrier();
-    const bf16x8 (*kv)[64] = s_kv[k & 1];
-    const int c = c_begin + k;
-    // S^T = K Q^T for both pages
-    f32x4 sacc[2][NT];
+  // S^T = K Q^T for both pages of chunk k
+  auto qk = [&](int k, f32x4 (&sacc)[2][NT]) {
+    const bf16x8 (*kv)[64] = s_kv[k % NB];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
 #pragma unroll
@@ -1267,31 +1282,40 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
             sacc[pg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[t][part][s], sacc[pg][t], 0, 0, 0);
       }
     }
-    // online softmax in log2 units with a lazy running max
-    const float fk0 = p.qk_scale_log2 * csk[0];
-    const float fk1 = p.qk_scale_log2 * csk[1];
-    const int key0 = c * kChunk + 4 * lq;  // key of register j: key0 + j (page 0), key0 + 16 + j (page 1)
-    const bool need_mask = (c * kChunk + kChunk - 1) >= first_masked_key;
-    bf16x8 pop_hi[NT], pop_lo[NT];
+  };
+
+  // Online softmax of one chunk in log2 units with a lazy running max: the
+  // max is taken on the raw scores of each page (the page's positive score
+  // factor keeps the order), and each weight comes out of one fma and one
+  // exp2 with the V scale already in it: P~ = 2^(s fk + log2 sV - base)
+  // = p sV.  The row sum adds P~ / sV = P~ 2^-log2 sV per page (the same
+  // rounding of log2 sV on both sides of the quotient).  P~ leaves as bf16
+  // hi + lo operands.
+  auto softmax = [&](int k, const ChunkMeta& ch, f32x4 (&sacc)[2][NT], bf16x8 (&pop_hi)[NT],
+                     bf16x8 (&pop_lo)[NT]) {
+    const int cu = __builtin_amdgcn_readfirstlane(c_begin + k);
+    const int key0 = cu * kChunk + 4 * lq;  // key of register j: key0 + j (page 0), key0 + 16 + j (page 1)
+    const bool need_mask = (cu * kChunk + kChunk - 1) >= first_masked_key;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] = sacc[0][t][j] * fk0;
-        x[4 + j] = sacc[1][t][j] * fk1;
-      }
       if (need_mask) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          x[j] = (key0 + j <= lim[t]) ? x[j] : kNegInf;
-          x[4 + j] = (key0 + 16 + j <= lim[t]) ? x[4 + j] : kNegInf;
+          sacc[0][t][j] = (key0 + j <= lim[t]) ? sacc[0][t][j] : kNegInf;
+          sacc[1][t][j] = (key0 + 16 + j <= lim[t]) ? sacc[1][t][j] : kNegInf;
         }
       }
-      float mx = x[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-      mx = max_over_lq(mx);
+      const float r0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[0][t][0], sacc[0][t][1]),
+                                                     __builtin_elementwise_maximum(sacc[0][t][2], sacc[0][t][3]));
+      const float r1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[1][t][0], sacc[1][t][1]),
+                                                     __builtin_elementwise_maximum(sacc[1][t][2], sacc[1][t][3]));
+      float mx = __builtin_elementwise_maximum(r0 * ch.fk[0], r1 * ch.fk[1]);
+      {
+        auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        auto c2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = __builtin_elementwise_maximum(__uint_as_float(c2[0]), __uint_as_float(c2[1]));
+      }
       if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyLog2)) {
         const float mn = fmaxf(m[t], mx);
         const float alpha = __builtin_amdgcn_exp2f(m[t] - ((mn == kNegInf) ? 0.f : mn));
@@ -1299,25 +1323,34 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
         for (int cb2 = 0; cb2 < GD::NVB; ++cb2) o[t][cb2] *= alpha;
         l[t] *= alpha;
         m[t] = mn;
+        base[t] = (mn == kNegInf) ? 0.f : mn;
       }
-      const float base = (m[t] == kNegInf) ? 0.f : m[t];
+      const float c0 = ch.lv[0] - base[t];
+      const float c1 = ch.lv[1] - base[t];
+      float pw[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pw[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][t][j], ch.fk[0], c0));
+        pw[4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][t][j], ch.fk[1], c1));
+      }
+      const float rs0 = (pw[0] + pw[1]) + (pw[2] + pw[3]);
+      const float rs1 = (pw[4] + pw[5]) + (pw[6] + pw[7]);
+      l[t] = __builtin_fmaf(rs1, __builtin_amdgcn_exp2f(-ch.lv[1]),
+                            __builtin_fmaf(rs0, __builtin_amdgcn_exp2f(-ch.lv[0]), l[t]));
       uint32_t phi[4], plo[4];
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
-        const float pa0 = __builtin_amdgcn_exp2f(x[2 * k2] - base);
-        const float pa1 = __builtin_amdgcn_exp2f(x[2 * k2 + 1] - base);
-        l[t] += pa0 + pa1;
-        // P~ = p * V scale as bf16 hi + lo
-        const float sc = (k2 < 2) ? csv[0] : csv[1];
-        const float a = pa0 * sc;
-        const float bb = pa1 * sc;
-        phi[k2] = pack_bf16(a, bb);
-        plo[k2] = pack_bf16(a - bf16_lo(phi[k2]), bb - bf16_hi(phi[k2]));
+        phi[k2] = pack_bf16(pw[2 * k2], pw[2 * k2 + 1]);
+        plo[k2] = pack_bf16(pw[2 * k2] - bf16_lo(phi[k2]), pw[2 * k2 + 1] - bf16_hi(phi[k2]));
       }
       pop_hi[t] = __builtin_bit_cast(bf16x8, u32x4{phi[0], phi[1], phi[2], phi[3]});
       pop_lo[t] = __builtin_bit_cast(bf16x8, u32x4{plo[0], plo[1], plo[2], plo[3]});
     }
-    // O^T += V^T P~^T
+  };
+
+  // O^T += V^T P~^T for chunk k
+  auto pv = [&](int k, const bf16x8 (&pop_hi)[NT], const bf16x8 (&pop_lo)[NT]) {
+    const bf16x8 (*kv)[64] = s_kv[k % NB];
 #pragma unroll
     for (int cblk = 0; cblk < GD::NVB; ++cblk) {
       const bf16x8 va = kv[TG::KSL + cblk][lane];
@@ -1329,7 +1362,55 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
     }
   };
 
-  ring_loop_split<R>(nk, issue, consume, compute);
+  // Ping-pong (PP): the waves of the first half (one per SIMD) issue their
+  // matrix work first and then the softmax, the second half the other way
+  // round, so that on every SIMD one wave's softmax runs beside the other's
+  // MFMAs.  First half, chunk k: PV of k - 1, QK of k, softmax of k.
+  // Second half: softmax and PV of k - 1, QK of k.  Both meet at the one
+  // barrier per chunk; each carries its chunk k - 1 work across it.
+  if constexpr (!PP) {
+    auto compute = [&](int k) {
+      lds_barrier();
+      f32x4 sacc[2][NT];
+      bf16x8 pop_hi[NT], pop_lo[NT];
+      qk(k, sacc);
+      softmax(k, cm, sacc, pop_hi, pop_lo);
+      pv(k, pop_hi, pop_lo);
+    };
+    ring_loop_split<R>(nk, issue, consume, compute);
+  } else if (TILE_PP_PARITY ? (wave % 2 == 0) : (wave < NW / 2)) {
+    // leading half: its P~ of chunk k - 1 crosses the barrier
+    bf16x8 pop_hi[NT], pop_lo[NT];
+    auto compute = [&](int k) {
+      lds_barrier();
+      if (k > 0) pv(k - 1, pop_hi, pop_lo);
+      f32x4 sacc[2][NT];
+      qk(k, sacc);
+      softmax(k, cm, sacc, pop_hi, pop_lo);
+    };
+    ring_loop_split<R>(nk, issue, consume, compute);
+    if (nk > 0) pv(nk - 1, pop_hi, pop_lo);
+  } else {
+    // lagging half: its scores of chunk k - 1 cross the barrier
+    f32x4 sacc[2][NT];
+    ChunkMeta cm_prev;
+    auto compute = [&](int k) {
+      lds_barrier();
+      if (k > 0) {
+        bf16x8 pop_hi[NT], pop_lo[NT];
+        softmax(k - 1, cm_prev, sacc, pop_hi, pop_lo);
+        pv(k - 1, pop_hi, pop_lo);
+      }
+      qk(k, sacc);
+      cm_prev = cm;
+    };
+    ring_loop_split<R>(nk, issue, consume, compute);
+    if (nk > 0) {
+      bf16x8 pop_hi[NT], pop_lo[NT];
+      softmax(nk - 1, cm_prev, sacc, pop_hi, pop_lo);
+      pv(nk - 1, pop_hi, pop_lo);
+    }
+  }
 
   // ---- write: final output, or this piece's partial -----------------------
 #pragma unroll
@@ -1506,6 +1587,7 @@ template <int NW, int NT>
 struct TileCfg {
   static constexpr int R = (NT == 2) ? TILE_RING_WIDE : (NW == 2 ? TILE_RING2 : TILE_RING4);
   static constexpr int WAVES_PER_SIMD = 2;
+  static constexpr bool PP = TILE_PINGPONG && NW == 8;
 };
 
 template <int D, int NW, int NT, bool QF32, bool OUTF32, bool KI8>
@@ -1521,7 +1603,7 @@ __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void at
   const int W = work_units(p, T);
   if (w >= W) return;
   walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
-    run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KI8>(p, pc, lane, wave);
+    run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KI8, TileCfg<NW, NT>::PP>(p, pc, lane, wave);
   });
 }
 
