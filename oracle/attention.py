@@ -24,6 +24,13 @@ Readings where the pages are silent (each listed in the design notes):
       v_pages [P][Hkv][S/4][D/64][16][4][4]: with NVB = D/16 and
         d = NVB*a + 4*i + e, the V byte of slot s, dim d is
         v[p][h][s // 4][i][a][e][s % 4].
+  * INT4 pools (two 4-bit codes per byte, D = 128), the library's layouts:
+      k_pages [P][Hkv][4][S][D/8]: with u = d % (D/4), the K code of slot s,
+        dim d is nibble u % 2 (0: bits 0-3, 1: bits 4-7) of
+        k[p][h][d // (D/4)][s][u // 2];
+      v_pages [P][Hkv][S/4][16][D/16][2]: with NVB = D/16 and d = NVB*a + r,
+        the V code of slot s, dim d is nibble s % 2 of
+        v[p][h][s // 4][a][r][(s % 4) // 2].
   * Scale 1/sqrt(D) unless given; no soft-cap, ALiBi, window or sinks.
   * Bytes past a sequence's length and unreferenced pages are never read.
 
@@ -68,6 +75,23 @@ def v_token_bytes(v_pages: np.ndarray, pages: np.ndarray, h: int, slots: np.ndar
     return parts.transpose(0, 2, 1, 3).reshape(parts.shape[0], -1)
 
 
+def k4_token_codes(k_pages: np.ndarray, pages: np.ndarray, h: int, slots: np.ndarray) -> np.ndarray:
+    """INT4 K codes (0..15) of (page, head h, slot) for each token: [T][D]."""
+    quarters = k_pages[pages, h, :, slots, :]  # [T][4][D/8] bytes
+    lo = quarters & 0x0F  # even u
+    hi = quarters >> 4  # odd u
+    codes = np.stack([lo, hi], axis=-1)  # [T][4][D/8][2]: u = 2 * byte + nibble
+    return codes.reshape(codes.shape[0], -1)
+
+
+def v4_token_codes(v_pages: np.ndarray, pages: np.ndarray, h: int, slots: np.ndarray) -> np.ndarray:
+    """INT4 V codes (0..15) of (page, head h, slot) for each token: [T][D]."""
+    pairs = v_pages[pages, h, slots // 4, :, :, (slots % 4) // 2]  # [T][16][NVB]: d = NVB * a + r
+    shift = (4 * (slots % 2)).astype(np.uint8)[:, None, None]
+    codes = (pairs >> shift) & 0x0F
+    return codes.reshape(codes.shape[0], -1)
+
+
 def softmax_scale(head_dim: int, sm_scale: float | None) -> float:
     return 1.0 / np.sqrt(head_dim) if not sm_scale else float(sm_scale)
 
@@ -81,12 +105,20 @@ class GatheredSequence:
     page_of_token: np.ndarray  # int64 [L]
 
 
-def gather_sequence(k_pages, v_pages, kv_scales, block_table_row, ctx_len: int) -> GatheredSequence:
-    """Follow one sequence's block table and collect its L tokens' bytes and scales."""
+def gather_sequence(k_pages, v_pages, kv_scales, block_table_row, ctx_len: int,
+                    kv_format: str = "e4m3") -> GatheredSequence:
+    """Follow one sequence's block table and collect its L tokens' codes
+    (bytes, or 4-bit codes for INT4) and scales."""
     k_pages = np.asarray(k_pages)
     v_pages = np.asarray(v_pages)
-    _, hkv, d_blocks, page_size, _ = k_pages.shape
-    d = 16 * d_blocks
+    if kv_format == "int4":
+        _, hkv, _, page_size, half_quarter = k_pages.shape
+        d = 8 * half_quarter
+        k_codes, v_codes = k4_token_codes, v4_token_codes
+    else:
+        _, hkv, d_blocks, page_size, _ = k_pages.shape
+        d = 16 * d_blocks
+        k_codes, v_codes = k_token_bytes, v_token_bytes
     t = np.arange(int(ctx_len))
     pages, slots = token_location(np.asarray(block_table_row).astype(np.int64), t, page_size)
     kb = np.empty((hkv, t.size, d), dtype=np.uint8)
@@ -94,8 +126,8 @@ def gather_sequence(k_pages, v_pages, kv_scales, block_table_row, ctx_len: int) 
     ks = np.empty((hkv, t.size), dtype=np.float64)
     vs = np.empty((hkv, t.size), dtype=np.float64)
     for h in range(hkv):
-        kb[h] = k_token_bytes(k_pages, pages, h, slots)
-        vb[h] = v_token_bytes(v_pages, pages, h, slots)
+        kb[h] = k_codes(k_pages, pages, h, slots)
+        vb[h] = v_codes(v_pages, pages, h, slots)
         ks[h] = kv_scales[0][pages, h]
         vs[h] = kv_scales[1][pages, h]
     return GatheredSequence(kb, vb, ks, vs, pages)
@@ -109,12 +141,22 @@ def decode_int8(codes) -> np.ndarray:
     return np.where(c < 128, c, c - 256).astype(np.float64)
 
 
+def decode_int4(codes) -> np.ndarray:
+    """INT4 KV codes (two's complement in 4 bits) -> fp64: code c is c for
+    c < 8, c - 16 otherwise (the quantisation section lists INT4 beside INT8
+    and FP8, with the same per-group scales)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0x0F
+    return np.where(c < 8, c, c - 16).astype(np.float64)
+
+
 def decode_kv(codes, kv_format: str = "e4m3") -> np.ndarray:
-    """KV bytes -> fp64 values before the page scale."""
+    """KV codes -> fp64 values before the page scale."""
     if kv_format == "e4m3":
         return e4m3.decode(codes)
     if kv_format == "int8":
         return decode_int8(codes)
+    if kv_format == "int4":
+        return decode_int4(codes)
     raise ValueError(kv_format)
 
 
@@ -142,7 +184,7 @@ def paged_attention(q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_len
         L, Q = int(ctx_lens[b]), int(q_lens[b])
         mine = [i for i in range(Q) if want is None or (row0 + i) in want]
         if mine:
-            g = gather_sequence(k_pages, v_pages, kv_scales, block_table[b], L)
+            g = gather_sequence(k_pages, v_pages, kv_scales, block_table[b], L, kv_format)
             k_deq = [decode_kv(g.k_bytes[h], kv_format) * g.k_scale[h][:, None] for h in range(num_kv_heads)]
             v_deq = [decode_kv(g.v_bytes[h], kv_format) * g.v_scale[h][:, None] for h in range(num_kv_heads)]
             idx = np.array(mine)

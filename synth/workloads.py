@@ -51,6 +51,7 @@ import torch
 PAGE_SIZE = 16
 E4M3_MAX = 448.0
 POISON_BYTE = 0x7F
+INT4_POISON = 0x8  # the 4-bit code of -8: never produced by the INT4 quantiser
 
 
 @dataclass
@@ -76,7 +77,8 @@ class Workload:
     seed: int = 0
     # Per-sequence logical (unpaged) copies of the quantised K/V, for tests.
     logical: list = field(default_factory=list, repr=False)
-    kv_format: str = "e4m3"  # or "int8": two's-complement bytes, scale = absmax / 127
+    kv_format: str = "e4m3"  # "int8": two's-complement bytes, scale = absmax / 127; "int4": 4-bit codes,
+    # two per byte, scale = absmax / 7 (the logical copies then hold one code per uint8)
 
     @property
     def num_seqs(self) -> int:
@@ -141,6 +143,52 @@ def _quantise_pages_int8(x: np.ndarray, valid_slots: np.ndarray):
     codes = np.clip(np.rint(y), -127, 127).astype(np.int8).view(np.uint8)
     codes = np.where(slot_ok[:, None, :, None], codes, np.uint8(POISON_BYTE)).astype(np.uint8)
     return codes, scale
+
+
+def _quantise_pages_int4(x: np.ndarray, valid_slots: np.ndarray):
+    """INT4 variant of _quantise_pages: scale = fp32(absmax) / 7 (1.0 if
+    absmax is 0), code = round-half-even of fp32(x / scale) clipped to +-7,
+    kept as its 4-bit two's complement (0..15, one per uint8); unused slots
+    hold the code of -8, which the quantiser never produces."""
+    n, hkv, s, d = x.shape
+    slot_ok = np.arange(s)[None, :] < valid_slots[:, None]
+    masked = np.where(slot_ok[:, None, :, None], np.abs(x), np.float32(0))
+    absmax = masked.reshape(n, hkv, s * d).max(axis=2).astype(np.float32)
+    scale = (absmax / np.float32(7.0)).astype(np.float32)
+    scale = np.where(absmax > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = (x / scale[:, :, None, None]).astype(np.float32)
+    codes = (np.clip(np.rint(y), -7, 7).astype(np.int8).view(np.uint8) & 0x0F).astype(np.uint8)
+    codes = np.where(slot_ok[:, None, :, None], codes, np.uint8(INT4_POISON)).astype(np.uint8)
+    return codes, scale
+
+
+def empty_pages4(num_pages: int, num_kv_heads: int, head_dim: int):
+    """INT4 K and V pools in the ABI layouts (two codes per byte), every code -8."""
+    if head_dim != 128:
+        raise ValueError("INT4 pools are laid out for head_dim 128")
+    S = PAGE_SIZE
+    byte = np.uint8(INT4_POISON | (INT4_POISON << 4))
+    k = np.full((num_pages, num_kv_heads, 4, S, head_dim // 8), byte, dtype=np.uint8)
+    v = np.full((num_pages, num_kv_heads, S // 4, 16, head_dim // 16, 2), byte, dtype=np.uint8)
+    return k, v
+
+
+def k4_to_layout(codes: np.ndarray) -> np.ndarray:
+    """[N][Hkv][S][D] 4-bit codes -> [N][Hkv][4][S][D/8] bytes: quarter c of d
+    (d = c D/4 + u) holds u = 2 j (low nibble) and u = 2 j + 1 (high) in byte j."""
+    n, hkv, s, d = codes.shape
+    x = codes.reshape(n, hkv, s, 4, d // 8, 2).transpose(0, 1, 3, 2, 4, 5)  # [n][h][c][s][j][bit]
+    return np.ascontiguousarray((x[..., 0] | (x[..., 1] << 4)).astype(np.uint8))
+
+
+def v4_to_layout(codes: np.ndarray) -> np.ndarray:
+    """[N][Hkv][S][D] 4-bit codes -> [N][Hkv][S/4][16][D/16][2] bytes: slot
+    s = 4 g + 2 k + bit, d = (D/16) a + r; byte [g][a][r][k] holds bit 0 low."""
+    n, hkv, s, d = codes.shape
+    nvb = d // 16
+    x = codes.reshape(n, hkv, s // 4, 2, 2, 16, nvb)  # [n][h][g][k][bit][a][r]
+    x = x.transpose(0, 1, 2, 5, 6, 3, 4)  # [n][h][g][a][r][k][bit]
+    return np.ascontiguousarray((x[..., 0] | (x[..., 1] << 4)).astype(np.uint8))
 
 
 def empty_pages(num_pages: int, num_kv_heads: int, head_dim: int):
@@ -226,18 +274,19 @@ def build_workload(
         valid[first[b] : first[b] + n] = v
 
     k_f = rng.standard_normal((used, num_kv_heads, S, head_dim), dtype=np.float32)
-    quantise = _quantise_pages_int8 if kv_format == "int8" else _quantise_pages
+    quantise = {"int8": _quantise_pages_int8, "int4": _quantise_pages_int4}.get(kv_format, _quantise_pages)
     k_codes, k_scale = quantise(k_f, valid)
     del k_f
     v_f = rng.standard_normal((used, num_kv_heads, S, head_dim), dtype=np.float32)
     v_codes, v_scale = quantise(v_f, valid)
     del v_f
 
-    k_pages, v_pages = empty_pages(num_pages, num_kv_heads, head_dim)
+    int4 = kv_format == "int4"
+    k_pages, v_pages = (empty_pages4 if int4 else empty_pages)(num_pages, num_kv_heads, head_dim)
     kv_scales = np.full((2, num_pages, num_kv_heads), np.nan, dtype=np.float32)
     used_phys = phys[:used]
-    k_pages[used_phys] = k_to_layout(k_codes)
-    v_pages[used_phys] = v_to_layout(v_codes)
+    k_pages[used_phys] = (k4_to_layout if int4 else k_to_layout)(k_codes)
+    v_pages[used_phys] = (v4_to_layout if int4 else v_to_layout)(v_codes)
     kv_scales[0, used_phys] = k_scale
     kv_scales[1, used_phys] = v_scale
 

@@ -49,6 +49,13 @@ def int8_by_torch(codes) -> np.ndarray:
     return t.view(torch.int8).to(torch.float64).numpy()
 
 
+def int4_by_shift(codes) -> np.ndarray:
+    """4-bit two's-complement codes read by moving the nibble to the top of
+    an int8 and shifting it back arithmetically (sign extension)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (((c & 0x0F) << 4).astype(np.uint8).view(np.int8) >> 4).astype(np.float64)
+
+
 def e4m3_by_torch(codes) -> np.ndarray:
     t = torch.as_tensor(np.asarray(codes, dtype=np.uint8))
     return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -63,10 +70,30 @@ def brute_force_attention(w) -> np.ndarray:
     ksc = w.kv_scales[0].reshape(-1).tolist()
     vsc = w.kv_scales[1].reshape(-1).tolist()
     q = w.q.double().numpy()
-    if getattr(w, "kv_format", "e4m3") == "int8":
+    fmt = getattr(w, "kv_format", "e4m3")
+    if fmt == "int8":
         dec = [float(c - 256 if c & 0x80 else c) for c in range(256)]  # two's complement
+    elif fmt == "int4":
+        dec = [float(c - 16 if c & 0x8 else c) for c in range(16)]
     else:
         dec = [e4m3_by_bits(c) for c in range(256)]
+
+    def k_code(p, h, s, d):
+        if fmt != "int4":
+            return kflat[(((p * Hkv + h) * (D // 16) + d // 16) * S + s) * 16 + d % 16]
+        # [P][Hkv][4][S][D/8], nibble u % 2 of byte u // 2 with u = d % (D/4)
+        u = d % (D // 4)
+        byte = kflat[(((p * Hkv + h) * 4 + d // (D // 4)) * S + s) * (D // 8) + u // 2]
+        return (byte >> (4 * (u % 2))) & 0xF
+
+    def v_code(p, h, s, d):
+        nvb = D // 16
+        if fmt != "int4":
+            va, vi, ve = d // nvb, (d % nvb) // 4, d % 4
+            return vflat[(((((p * Hkv + h) * (S // 4) + s // 4) * (D // 64) + vi) * 16 + va) * 4 + ve) * 4 + s % 4]
+        # [P][Hkv][S/4][16][D/16][2], nibble s % 2 of byte (s % 4) // 2, d = nvb a + r
+        byte = vflat[(((((p * Hkv + h) * (S // 4) + s // 4) * 16 + d // nvb) * nvb + d % nvb) * 2 + (s % 4) // 2)]
+        return (byte >> (4 * (s % 2))) & 0xF
     scale = w.sm_scale if w.sm_scale else 1.0 / math.sqrt(D)
     out = np.zeros(q.shape, dtype=np.float64)
     row = 0
@@ -82,8 +109,7 @@ def brute_force_attention(w) -> np.ndarray:
                     s = t % S
                     acc = 0.0
                     for d in range(D):
-                        kb = kflat[(((p * Hkv + h) * (D // 16) + d // 16) * S + s) * 16 + d % 16]
-                        acc += float(q[row + i, hq, d]) * dec[kb] * ksc[p * Hkv + h]
+                        acc += float(q[row + i, hq, d]) * dec[k_code(p, h, s, d)] * ksc[p * Hkv + h]
                     zs.append(acc * scale)
                 zmax = max(zs)
                 ws = [math.exp(z - zmax) for z in zs]
@@ -93,11 +119,7 @@ def brute_force_attention(w) -> np.ndarray:
                     for t in range(position + 1):
                         p = int(w.block_table[b][t // S])
                         s = t % S
-                        nvb = D // 16
-                        va, vi, ve = d // nvb, (d % nvb) // 4, d % 4
-                        vb = vflat[(((((p * Hkv + h) * (S // 4) + s // 4) * (D // 64) + vi) * 16 + va) * 4 + ve) * 4
-                                   + s % 4]
-                        acc += ws[t] * dec[vb] * vsc[p * Hkv + h]
+                        acc += ws[t] * dec[v_code(p, h, s, d)] * vsc[p * Hkv + h]
                     out[row + i, hq, d] = acc / tot
         row += Q
     return out
@@ -113,7 +135,7 @@ def sdpa_attention(w) -> np.ndarray:
     for b in range(w.num_seqs):
         L, Q = int(w.ctx_lens[b]), int(w.q_lens[b])
         lg = w.logical[b]
-        dec = int8_by_torch if getattr(w, "kv_format", "e4m3") == "int8" else e4m3_by_torch
+        dec = {"int8": int8_by_torch, "int4": int4_by_shift}.get(getattr(w, "kv_format", "e4m3"), e4m3_by_torch)
         k = torch.from_numpy(dec(lg["k_bytes"]) * lg["k_scale"][:, :, None].astype(np.float64))
         v = torch.from_numpy(dec(lg["v_bytes"]) * lg["v_scale"][:, :, None].astype(np.float64))
         qb = q_all[row : row + Q].permute(1, 0, 2).contiguous()  # [Hq][Q][D]
