@@ -82,8 +82,8 @@ def test_planted_table_bias_is_caught(bias, monkeypatch):
 def test_planted_swapped_scales_are_caught(monkeypatch):
     real = pa.gather_sequence
 
-    def swapped(k_pages, v_pages, kv_scales, row, L):
-        return real(k_pages, v_pages, kv_scales[::-1], row, L)
+    def swapped(k_pages, v_pages, kv_scales, row, L, *fmt):
+        return real(k_pages, v_pages, kv_scales[::-1], row, L, *fmt)
 
     monkeypatch.setattr(pa, "gather_sequence", swapped)
     ok, _ = _all_pins_pass()
@@ -93,8 +93,8 @@ def test_planted_swapped_scales_are_caught(monkeypatch):
 def test_planted_dropped_scale_is_caught(monkeypatch):
     real = pa.gather_sequence
 
-    def unscaled(k_pages, v_pages, kv_scales, row, L):
-        return real(k_pages, v_pages, np.ones_like(kv_scales), row, L)
+    def unscaled(k_pages, v_pages, kv_scales, row, L, *fmt):
+        return real(k_pages, v_pages, np.ones_like(kv_scales), row, L, *fmt)
 
     monkeypatch.setattr(pa, "gather_sequence", unscaled)
     ok, _ = _all_pins_pass()
