@@ -60,7 +60,8 @@ def algorithmic_counts(w) -> dict:
     L = w.ctx_lens.astype(np.int64)
     Q = w.q_lens.astype(np.int64)
     pages = (L + w.page_size - 1) // w.page_size
-    kv = int((L * w.num_kv_heads * w.head_dim * 2).sum())
+    code_bytes = 0.5 if getattr(w, "kv_format", "e4m3") == "int4" else 1  # two INT4 codes per byte
+    kv = int((L * w.num_kv_heads * w.head_dim * 2 * code_bytes).sum())
     scales = int((pages * w.num_kv_heads * 8).sum())
     bt = int((pages * 4).sum())
     qb = 4 if w.q_dtype == "f32" else 2
@@ -208,8 +209,9 @@ def workload_config(w) -> dict:
         "ctx_min": int(w.ctx_lens.min()),
         "ctx_max": int(w.ctx_lens.max()),
         "ctx_mean": float(w.ctx_lens.mean()),
-        "kv_format": ("int8 (two's complement), fp32 scale per (page, kv head)" if w.kv_format == "int8"
-                      else "fp8_e4m3 (OCP), fp32 scale per (page, kv head)"),
+        "kv_format": {"int8": "int8 (two's complement), fp32 scale per (page, kv head)",
+                      "int4": "int4 (two's complement, two per byte), fp32 scale per (page, kv head)"}.get(
+                          w.kv_format, "fp8_e4m3 (OCP), fp32 scale per (page, kv head)"),
         "q_dtype": w.q_dtype,
         "out_dtype": w.out_dtype,
         "seed": w.seed,
@@ -250,7 +252,8 @@ def counter_summary_path(workload: str, kernel: str = "attn_stream_kernel") -> s
 
 def profile_name(w) -> str:
     """Workload name of a counter summary: INT8-KV runs have their own."""
-    return w.name + ("_int8" if getattr(w, "kv_format", "e4m3") == "int8" else "")
+    fmt = getattr(w, "kv_format", "e4m3")
+    return w.name + ("" if fmt == "e4m3" else "_" + fmt)
 
 
 def committed_traffic(workload: str, kernel: str = "attn_stream_kernel"):
@@ -488,7 +491,8 @@ def cpu_baseline(w, counts, budget_s: float) -> dict:
     pages = (L + w.page_size - 1) // w.page_size
     qb = 4 if w.q_dtype == "f32" else 2
     ob = 4 if w.out_dtype == "f32" else 2
-    per_seq_bytes = (L * w.num_kv_heads * w.head_dim * 2 + pages * w.num_kv_heads * 8 + pages * 4
+    code_bytes = 0.5 if getattr(w, "kv_format", "e4m3") == "int4" else 1
+    per_seq_bytes = (L * w.num_kv_heads * w.head_dim * 2 * code_bytes + pages * w.num_kv_heads * 8 + pages * 4
                      + w.q_lens.astype(np.int64) * w.num_q_heads * w.head_dim * (qb + ob) + 8)
     b = 0
     while True:
@@ -536,8 +540,9 @@ def main():
     ap.add_argument("--stream-calibration", action="store_true",
                     help="measure the streaming-read ceiling over random chunks of 1-64 KB (attn_calib_stream_read)")
     ap.add_argument("--summary-out", default=None, help="with --stream-calibration: write the text summary here")
-    ap.add_argument("--kv-format", default="e4m3", choices=["e4m3", "int8"],
-                    help="KV byte format of the attention workloads (INT8: two's complement times the page scale)")
+    ap.add_argument("--kv-format", default="e4m3", choices=["e4m3", "int8", "int4"],
+                    help="KV format of the attention workloads (INT8: two's-complement bytes times the page "
+                         "scale; INT4: two 4-bit codes per byte, attention workloads of head_dim 128 only)")
     ap.add_argument("--json-out", default=None)
     args = ap.parse_args()
 

@@ -94,8 +94,18 @@ typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype_t;
  * integer times the page's scale (the same scales, layouts and rules as
  * E4M3 otherwise).  INT8 plans take BF16 q and out; attn_kv_append on an
  * INT8 plan uses 127 in place of 448 and the integer nearest to
- * value / scale (ties to even, clipped to +-127). */
-typedef enum { ATTN_KV_E4M3 = 0, ATTN_KV_INT8 = 1 } attn_kv_format_t;
+ * value / scale (ties to even, clipped to +-127).
+ * With ATTN_KV_INT4 (head_dim 128, BF16 q and out) every byte holds two
+ * 4-bit two's-complement codes in [-8, 7], code j of a byte in bits 4j..4j+3,
+ * and a value is its code times the page's scale; a (page, kv head) chunk is
+ * 1 KB of K and 1 KB of V:
+ *   k_pages  uint8 [P][Hkv][4][16][D/8]: with u = d % 32, the K code of
+ *            slot s, dim d is code u % 2 of byte [d / 32][s][u / 2]
+ *   v_pages  uint8 [P][Hkv][4][16][D/16][2]: with d = (D/16)*a + r, the V
+ *            code of slot s, dim d is code s % 2 of byte [s / 4][a][r][(s % 4) / 2]
+ * (16 consecutive bytes hold one lane's MFMA operand codes).
+ * attn_kv_append does not write INT4 pools (ATTN_ERR_UNSUPPORTED). */
+typedef enum { ATTN_KV_E4M3 = 0, ATTN_KV_INT8 = 1, ATTN_KV_INT4 = 2 } attn_kv_format_t;
 
 /* Static shape of the work a plan serves (the "adaptive tiling" of the
  * attention section: tile and split sizes are chosen from it once). */
@@ -117,7 +127,7 @@ typedef struct {
                                 cut into segments * n equal contiguous
                                 partitions (so each of equal-length segments
                                 gets exactly n), merged by log-sum-exp */
-  int32_t kv_format;         /* ATTN_KV_E4M3 (0) or ATTN_KV_INT8 (1) */
+  int32_t kv_format;         /* ATTN_KV_E4M3 (0), ATTN_KV_INT8 (1) or ATTN_KV_INT4 (2) */
   int32_t reserved[3];       /* must be zero */
 } attn_plan_desc_t;
 
@@ -313,6 +323,13 @@ attn_status_t attn_debug_decode_fp8(const uint8_t* in, float* out, int64_t n, hi
  * device memory, out 4-byte aligned.  n >= 0; n == 0 enqueues nothing;
  * n < 0 or a null pointer -> ATTN_ERR_INVALID_ARGUMENT. */
 attn_status_t attn_debug_decode_int8(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
+
+/* out[2i + j] = the value of code j (bits 4j..4j+3, two's complement) of
+ * byte in[i] as the attention kernels widen it for ATTN_KV_INT4 pools (the
+ * page scale is not applied).  in: n bytes, out: 2n floats, both device
+ * memory, out 4-byte aligned.  n >= 0; n == 0 enqueues nothing; n < 0 or a
+ * null pointer -> ATTN_ERR_INVALID_ARGUMENT. */
+attn_status_t attn_debug_decode_int4(const uint8_t* in, float* out, int64_t n, hipStream_t stream);
 
 /* out[i] = the E4M3 byte of fp32 in[i] as the append kernel encodes it
  * (nearest code, ties to even, magnitudes above 448 saturated, sign kept;

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     PlanInfo,
     calib_stream_read,
     debug_decode_fp8,
+    debug_decode_int4,
     debug_decode_int8,
     debug_encode_fp8,
     debug_gather,

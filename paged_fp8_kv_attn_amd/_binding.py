@@ -31,6 +31,7 @@ _FUNCTIONS = [
     "attn_debug_gather",
     "attn_debug_decode_fp8",
     "attn_debug_decode_int8",
+    "attn_debug_decode_int4",
     "attn_kv_append",
     "attn_debug_encode_fp8",
     "attn_mtp_accept_workspace_size",
@@ -131,6 +132,8 @@ def load_library():
     lib.attn_debug_decode_fp8.restype = i32
     lib.attn_debug_decode_int8.argtypes = [vp, vp, i64, vp]
     lib.attn_debug_decode_int8.restype = i32
+    lib.attn_debug_decode_int4.argtypes = [vp, vp, i64, vp]
+    lib.attn_debug_decode_int4.restype = i32
     lib.attn_kv_append.argtypes = [vp, vp, vp, i32] + [vp] * 7
     lib.attn_kv_append.restype = i32
     lib.attn_debug_encode_fp8.argtypes = [vp, vp, i64, vp]
@@ -194,6 +197,13 @@ def _dtype_code(dt) -> int:
 
 
 _TORCH_OF = {ATTN_DTYPE_F32: torch.float32, ATTN_DTYPE_BF16: torch.bfloat16}
+KV_FORMATS = {"e4m3": 0, "int8": 1, "int4": 2}
+
+
+def _chunk_bytes(desc) -> int:
+    """Bytes of one (page, kv head) chunk of a pool: 16 slots x D codes, two
+    codes per byte for INT4."""
+    return desc.page_size * desc.head_dim // (2 if desc.kv_format == 2 else 1)
 
 
 def _want(t, name: str, device, dtypes, min_numel: int = 0, numel: int | None = None):
@@ -228,7 +238,7 @@ def check_forward_tensors(desc: "PlanDesc", device, q, k_pages, v_pages, kv_scal
     stays a precondition: it must not exceed q's rows."""
     d = desc
     row = d.num_q_heads * d.head_dim
-    chunk = d.num_pages * d.num_kv_heads * d.page_size * d.head_dim
+    chunk = d.num_pages * d.num_kv_heads * _chunk_bytes(d)
     _want(q, "q", device, (_TORCH_OF[d.q_dtype],), min_numel=d.num_seqs * row)
     if q.numel() % row or q.numel() > d.num_seqs * d.max_q_len * row:
         raise ValueError(f"q: {q.numel()} elements is not a whole number of rows of Hq x D = {row} "
@@ -247,7 +257,7 @@ def check_append_tensors(desc: "PlanDesc", device, k_new, v_new, k_pages, v_page
     """The checks Plan.kv_append makes before calling attn_kv_append."""
     d = desc
     row = d.num_kv_heads * d.head_dim
-    chunk = d.num_pages * d.num_kv_heads * d.page_size * d.head_dim
+    chunk = d.num_pages * d.num_kv_heads * _chunk_bytes(d)
     _want(k_new, "k_new", device, (torch.bfloat16, torch.float32), min_numel=d.num_seqs * row)
     _want(v_new, "v_new", device, (k_new.dtype,), numel=k_new.numel())
     if k_new.numel() % row or k_new.numel() > d.num_seqs * d.max_q_len * row:
@@ -279,7 +289,7 @@ def make_desc(*, num_seqs, num_q_heads, num_kv_heads, head_dim, num_pages, max_p
     d.out_dtype = _dtype_code(out_dtype)
     d.sm_scale = float(sm_scale)
     d.num_kv_splits = num_kv_splits
-    d.kv_format = {"e4m3": 0, "int8": 1}.get(kv_format, kv_format) if isinstance(kv_format, str) else kv_format
+    d.kv_format = KV_FORMATS.get(kv_format, kv_format) if isinstance(kv_format, str) else kv_format
     for i, r in enumerate(reserved):
         d.reserved[i] = r
     return d
@@ -375,7 +385,7 @@ class Plan:
 def debug_gather(plan: Plan, k_pages, v_pages, kv_scales, block_table, ctx_lens, k_out, v_out, scale_out,
                  page_out, stream=None):
     d, dev = plan.desc, plan.device
-    chunk = d.num_pages * d.num_kv_heads * d.page_size * d.head_dim
+    chunk = d.num_pages * d.num_kv_heads * _chunk_bytes(d)
     per_tok = d.num_seqs * d.num_kv_heads * d.max_ctx_len
     _want(k_pages, "k_pages", dev, (torch.uint8,), min_numel=chunk)
     _want(v_pages, "v_pages", dev, (torch.uint8,), min_numel=chunk)
@@ -408,6 +418,16 @@ def debug_decode_int8(codes, out, stream=None):
     _check_codec(codes, (torch.uint8, torch.int8), out, (torch.float32,))
     st = load_library().attn_debug_decode_int8(_ptr(codes), _ptr(out), int(codes.numel()), _stream(stream))
     _check(st, "attn_debug_decode_int8")
+    return out
+
+
+def debug_decode_int4(codes, out, stream=None):
+    """Two INT4 codes per byte of `codes` (low nibble first) -> 2n floats as
+    the attention kernels widen them (attn_debug_decode_int4)."""
+    _want(codes, "input", None, (torch.uint8,))
+    _want(out, "out", codes.device, (torch.float32,), min_numel=2 * codes.numel())
+    st = load_library().attn_debug_decode_int4(_ptr(codes), _ptr(out), int(codes.numel()), _stream(stream))
+    _check(st, "attn_debug_decode_int4")
     return out
 
 

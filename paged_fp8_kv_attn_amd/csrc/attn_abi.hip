@@ -92,9 +92,11 @@ attn_status_t validate_desc(const attn_plan_desc_t& d) {
   if (d.out_dtype != ATTN_DTYPE_F32 && d.out_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARGUMENT;
   if (!(d.sm_scale >= 0.f) || !std::isfinite(d.sm_scale)) return ATTN_ERR_INVALID_ARGUMENT;
   if (d.num_kv_splits < 0) return ATTN_ERR_INVALID_ARGUMENT;
-  if (d.kv_format != ATTN_KV_E4M3 && d.kv_format != ATTN_KV_INT8) return ATTN_ERR_INVALID_ARGUMENT;
-  if (d.kv_format == ATTN_KV_INT8 && (d.q_dtype != ATTN_DTYPE_BF16 || d.out_dtype != ATTN_DTYPE_BF16))
+  if (d.kv_format != ATTN_KV_E4M3 && d.kv_format != ATTN_KV_INT8 && d.kv_format != ATTN_KV_INT4)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.kv_format != ATTN_KV_E4M3 && (d.q_dtype != ATTN_DTYPE_BF16 || d.out_dtype != ATTN_DTYPE_BF16))
     return ATTN_ERR_UNSUPPORTED;
+  if (d.kv_format == ATTN_KV_INT4 && d.head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (d.page_size != pa::kPageSize) return ATTN_ERR_UNSUPPORTED;
   if (d.head_dim != 64 && d.head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(d.max_pages_per_seq) * d.page_size < d.max_ctx_len) return ATTN_ERR_INVALID_ARGUMENT;
@@ -116,7 +118,7 @@ attn_status_t choose_plan(const attn_plan_desc_t& d, int device, attn_plan_s* p)
   v.head_dim = d.head_dim;
   v.q_f32 = d.q_dtype == ATTN_DTYPE_F32;
   v.out_f32 = d.out_dtype == ATTN_DTYPE_F32;
-  v.kv_int8 = d.kv_format == ATTN_KV_INT8;
+  v.kv_format = d.kv_format;
   if (cols <= 4) {  // four pages per score tile
     v.col_tiles = 1;
     v.packed = true;
@@ -495,6 +497,7 @@ attn_status_t attn_debug_gather(attn_plan_t plan, const uint8_t* k_pages, const 
   gp.bt_stride = d.max_pages_per_seq;
   gp.max_ctx_len = d.max_ctx_len;
   gp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
+  gp.kv_format = d.kv_format;
   const hipError_t e = pa::launch_debug_gather(gp, stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
@@ -511,6 +514,7 @@ attn_status_t attn_kv_append(attn_plan_t plan, const void* k_new, const void* v_
   const attn_status_t dst = check_device(plan);
   if (dst != ATTN_OK) return dst;
   const attn_plan_desc_t& d = plan->desc;
+  if (d.kv_format == ATTN_KV_INT4) return ATTN_ERR_UNSUPPORTED;
   pa::AppendParams ap{};
   ap.k_new = k_new;
   ap.v_new = v_new;
@@ -594,7 +598,7 @@ attn_status_t attn_debug_decode_fp8(const uint8_t* in, float* out, int64_t n, hi
   if (n < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (n == 0) return ATTN_OK;
   if (!in || !out || !aligned(out, 4)) return ATTN_ERR_INVALID_ARGUMENT;
-  const hipError_t e = pa::launch_debug_decode(in, out, n, false, stream);
+  const hipError_t e = pa::launch_debug_decode(in, out, n, pa::kKvE4M3, stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
@@ -602,7 +606,15 @@ attn_status_t attn_debug_decode_int8(const uint8_t* in, float* out, int64_t n, h
   if (n < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (n == 0) return ATTN_OK;
   if (!in || !out || !aligned(out, 4)) return ATTN_ERR_INVALID_ARGUMENT;
-  const hipError_t e = pa::launch_debug_decode(in, out, n, true, stream);
+  const hipError_t e = pa::launch_debug_decode(in, out, n, pa::kKvInt8, stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+attn_status_t attn_debug_decode_int4(const uint8_t* in, float* out, int64_t n, hipStream_t stream) {
+  if (n < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (n == 0) return ATTN_OK;
+  if (!in || !out || !aligned(out, 4)) return ATTN_ERR_INVALID_ARGUMENT;
+  const hipError_t e = pa::launch_debug_decode(in, out, n, pa::kKvInt4, stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

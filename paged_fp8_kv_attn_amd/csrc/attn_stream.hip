@@ -77,6 +77,75 @@ struct Geo {
   static constexpr int NVV = NVB / 4;   // 16-byte V loads per lane per page
 };
 
+// Loads of one page's K and V per lane: 16-byte loads; INT4 chunks are half
+// as large, one load each.
+template <int D, int KF>
+struct KvLoads {
+  static constexpr int NK = KF == kKvInt4 ? 1 : Geo<D>::NKV;
+  static constexpr int NV = KF == kKvInt4 ? 1 : Geo<D>::NVV;
+  static_assert(KF != kKvInt4 || D == 128, "INT4 pools are laid out for head_dim 128");
+};
+
+// Byte offset of a (page, kv head) chunk in the pool of format KF.
+template <int D, int KF>
+__device__ __forceinline__ uint64_t chunk_base(int32_t page, int head, int num_kv_heads) {
+  if constexpr (KF == kKvInt4) return chunk_offset4(page, head, num_kv_heads, D);
+  return chunk_offset(page, head, num_kv_heads, D);
+}
+
+// Lane (lq, ln)'s byte offset of K load i / V load i inside a chunk.
+template <int D, int KF>
+__device__ __forceinline__ uint32_t k_lane_off(int lq, int ln, int i) {
+  if constexpr (KF == kKvInt4) return lane_in_chunk4(lq, ln);
+  return k_in_chunk(ln, lq * Geo<D>::DQ + 16 * i, D);
+}
+template <int D, int KF>
+__device__ __forceinline__ uint32_t v_lane_off(int lq, int ln, int i) {
+  if constexpr (KF == kKvInt4) return lane_in_chunk4(lq, ln);
+  return v_in_chunk(4 * lq, Geo<D>::NVB * ln + 4 * i, D);
+}
+
+// K operand of slab s (8 values of d in the contraction order of the Q
+// operand) from a lane's K loads of one page.
+template <int D, int KF>
+__device__ __forceinline__ bf16x8 k_slab(const u32x4 (&kl)[KvLoads<D, KF>::NK], int s) {
+  if constexpr (KF == kKvInt4) {
+    return i4x8_to_bf16x8(kl[0][s]);
+  } else {
+    const u32x4 w = kl[(2 * s) / 4];
+    return kv8x8_to_bf16x8<KF == kKvInt8>(w[(2 * s) % 4], w[(2 * s) % 4 + 1]);
+  }
+}
+
+// The four slots of d-block cblk in a lane's V loads of one page: four
+// bytes, or four 4-bit codes (the low 16 bits) for INT4.
+template <int D, int KF>
+__device__ __forceinline__ uint32_t v_word(const u32x4 (&vl)[KvLoads<D, KF>::NV], int cblk) {
+  if constexpr (KF == kKvInt4) return (vl[0][cblk >> 1] >> (16 * (cblk & 1))) & 0xFFFFu;
+  return vl[cblk / 4][cblk % 4];
+}
+
+// Bits of slot j (< 4) in a four-slot word.
+template <int KF>
+__device__ __forceinline__ uint32_t slot_bits(int j) {
+  return KF == kKvInt4 ? (0xFu << (4 * j)) : (0xFFu << (8 * j));
+}
+
+// Four-slot words -> bf16: one page (4 values) or two pages (8 values).
+template <int KF>
+__device__ __forceinline__ bf16x4 v4_to_bf16(uint32_t w) {
+  if constexpr (KF == kKvInt4) return i4x4_to_bf16x4(w);
+  return kv8x4_to_bf16x4<KF == kKvInt8>(w);
+}
+template <int KF>
+__device__ __forceinline__ bf16x8 v8_to_bf16(uint32_t w0, uint32_t w1) {
+  if constexpr (KF == kKvInt4) {
+    const bf16x4 a = i4x4_to_bf16x4(w0), b = i4x4_to_bf16x4(w1);
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  return kv8x8_to_bf16x8<KF == kKvInt8>(w0, w1);
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kChunk = 32;  // keys per chunk (two pages)
 
@@ -312,9 +381,10 @@ struct PieceDesc {
   int slot;            // partial slot when not whole
 };
 
-template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int NBUF, bool KI8>
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int NBUF, int KF>
 __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc& pc, int lane, int wave) {
   using GD = Geo<D>;
+  using KL = KvLoads<D, KF>;
   constexpr int NW = kWavesPerGroup;
   constexpr int NP = QF32 ? 3 : 1;
   const int lq = lane >> 4;
@@ -388,11 +458,11 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
   const int32_t* bt = p.block_table + (size_t)pc.b * p.bt_stride;
   // load i of a lane reads 16 bytes: K block d = lq*DQ + 16i of slot ln; V
   // values d = NVB*ln + 4i .. +3 of the slots 4lq..4lq+3
-  uint32_t koff[GD::NKV], voff[GD::NVV];
+  uint32_t koff[KL::NK], voff[KL::NV];
 #pragma unroll
-  for (int i = 0; i < GD::NKV; ++i) koff[i] = k_in_chunk(ln, lq * GD::DQ + 16 * i, D);
+  for (int i = 0; i < KL::NK; ++i) koff[i] = k_lane_off<D, KF>(lq, ln, i);
 #pragma unroll
-  for (int i = 0; i < GD::NVV; ++i) voff[i] = v_in_chunk(4 * lq, GD::NVB * ln + 4 * i, D);
+  for (int i = 0; i < KL::NV; ++i) voff[i] = v_lane_off<D, KF>(lq, ln, i);
   const uint8_t* kpool = p.k_pages;
   const uint8_t* vpool = p.v_pages;
 
@@ -417,22 +487,22 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
       const int pg = min(2 * c + (lane & 1), npages - 1);  // a missing second page repeats the first
       ph = bt[pg];
       const int64_t sidx = (int64_t)ph * p.num_kv_heads + h;
-      a = p.kv_scales[sidx];
-      bsc = p.kv_scales[p.v_scale_offset + sidx];
+      a = p.kv_scales[sidx] * code_unit<KF>();
+      bsc = p.kv_scales[p.v_scale_offset + sidx] * code_unit<KF>();
     }
     bt_v = ph;
     sk_v = a;
     sv_v = bsc;
     settle_batch(bt_v, sk_v, sv_v);
   };
-  u32x4 kbuf[NBUF][2][GD::NKV], vbuf[NBUF][2][GD::NVV];
+  u32x4 kbuf[NBUF][2][KL::NK], vbuf[NBUF][2][KL::NV];
   float skb[NBUF][2], svb[NBUF][2];
   // fill ring slot j with chunk k (k < nk); a new batch of block-table
   // entries is fetched when k starts one (every chunk before k has already
   // been issued and has its scales latched)
   auto issue = [&](int k, int j) {
-    u32x4 (&kb)[2][GD::NKV] = kbuf[j];
-    u32x4 (&vb)[2][GD::NVV] = vbuf[j];
+    u32x4 (&kb)[2][KL::NK] = kbuf[j];
+    u32x4 (&vb)[2][KL::NV] = vbuf[j];
     float (&skj)[2] = skb[j];
     float (&svj)[2] = svb[j];
     if ((k & 31) == 0) load_batch(k);
@@ -440,12 +510,12 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       const int32_t ph = __builtin_amdgcn_readlane(bt_v, slot + pg);
-      const uint64_t base = chunk_offset(ph, h, p.num_kv_heads, D);
+      const uint64_t base = chunk_base<D, KF>(ph, h, p.num_kv_heads);
 #pragma unroll
-      for (int i = 0; i < GD::NKV; ++i)
+      for (int i = 0; i < KL::NK; ++i)
         kb[pg][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + base + koff[i]));
 #pragma unroll
-      for (int i = 0; i < GD::NVV; ++i)
+      for (int i = 0; i < KL::NV; ++i)
         vb[pg][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + base + voff[i]));
     }
     // the scales are read after the KV loads are issued: waiting for them
@@ -459,8 +529,8 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
 
   // compute chunk k from its ring slot
   auto step = [&](int k, int j) {
-    const u32x4 (&kc)[2][GD::NKV] = kbuf[j];
-    const u32x4 (&vc)[2][GD::NVV] = vbuf[j];
+    const u32x4 (&kc)[2][KL::NK] = kbuf[j];
+    const u32x4 (&vc)[2][KL::NV] = vbuf[j];
     const float (&skc)[2] = skb[j];
     const float (&svc)[2] = svb[j];
     const int c = c_begin + wave + k * NW;
@@ -472,8 +542,7 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
       for (int t = 0; t < NCT; ++t) sacc[pg][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < GD::NSLAB; ++s) {
-        const u32x4 w = kc[pg][(2 * s) / 4];
-        const bf16x8 kb = kv8x8_to_bf16x8<KI8>(w[(2 * s) % 4], w[(2 * s) % 4 + 1]);
+        const bf16x8 kb = k_slab<D, KF>(kc[pg], s);
 #pragma unroll
         for (int t = 0; t < NCT; ++t) {
 #pragma unroll
@@ -554,8 +623,8 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
       vmask1 = 0u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        vmask0 |= (key0 + j < L) ? (0xffu << (8 * j)) : 0u;
-        vmask1 |= (key0 + 16 + j < L) ? (0xffu << (8 * j)) : 0u;
+        vmask0 |= (key0 + j < L) ? slot_bits<KF>(j) : 0u;
+        vmask1 |= (key0 + 16 + j < L) ? slot_bits<KF>(j) : 0u;
       }
     }
     bf16x8 pop_hi[NCT], pop_lo[NCT];
@@ -566,9 +635,9 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
     }
 #pragma unroll
     for (int cblk = 0; cblk < GD::NVB; ++cblk) {
-      const uint32_t w0 = vc[0][cblk / 4][cblk % 4] & vmask0;
-      const uint32_t w1 = vc[1][cblk / 4][cblk % 4] & vmask1;
-      const bf16x8 va = kv8x8_to_bf16x8<KI8>(w0, w1);
+      const uint32_t w0 = v_word<D, KF>(vc[0], cblk) & vmask0;
+      const uint32_t w1 = v_word<D, KF>(vc[1], cblk) & vmask1;
+      const bf16x8 va = v8_to_bf16<KF>(w0, w1);
 #pragma unroll
       for (int t = 0; t < NCT; ++t) {
         o[t][cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi[t], o[t][cblk], 0, 0, 0);
@@ -713,9 +782,10 @@ __device__ __forceinline__ float dpp_ror8(float x) {
   return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x128 /*row_ror:8*/, 0xf, 0xf, false));
 }
 
-template <int D, bool QF32, bool OUTF32, int NRING, bool KI8>
+template <int D, bool QF32, bool OUTF32, int NRING, int KF>
 __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const PieceDesc& pc, int lane) {
   using GD = Geo<D>;
+  using KL = KvLoads<D, KF>;
   constexpr int NP = QF32 ? 3 : 1;
   const int lq = lane >> 4;
   const int ln = lane & 15;
@@ -780,11 +850,11 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
   const int32_t* bt = p.block_table + (size_t)pc.b * p.bt_stride;
   // load i of a lane reads 16 bytes: K block d = lq*DQ + 16i of slot ln; V
   // values d = NVB*ln + 4i .. +3 of the slots 4lq..4lq+3
-  uint32_t koff[GD::NKV], voff[GD::NVV];
+  uint32_t koff[KL::NK], voff[KL::NV];
 #pragma unroll
-  for (int i = 0; i < GD::NKV; ++i) koff[i] = k_in_chunk(ln, lq * GD::DQ + 16 * i, D);
+  for (int i = 0; i < KL::NK; ++i) koff[i] = k_lane_off<D, KF>(lq, ln, i);
 #pragma unroll
-  for (int i = 0; i < GD::NVV; ++i) voff[i] = v_in_chunk(4 * lq, GD::NVB * ln + 4 * i, D);
+  for (int i = 0; i < KL::NV; ++i) voff[i] = v_lane_off<D, KF>(lq, ln, i);
   const uint8_t* kpool = p.k_pages;
   const uint8_t* vpool = p.v_pages;
 
@@ -806,8 +876,8 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
       const int pg = min(2 * c + (lane & 3), npages - 1);  // missing pages repeat the last one
       ph = bt[pg];
       const int64_t sidx = (int64_t)ph * p.num_kv_heads + h;
-      a = p.kv_scales[sidx];
-      bsc = p.kv_scales[p.v_scale_offset + sidx];
+      a = p.kv_scales[sidx] * code_unit<KF>();
+      bsc = p.kv_scales[p.v_scale_offset + sidx] * code_unit<KF>();
     }
     bt_v = ph;
     sk_v = a;
@@ -815,11 +885,11 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
     settle_batch(bt_v, sk_v, sv_v);
   };
 
-  u32x4 kbuf[NRING][4][GD::NKV], vbuf[NRING][4][GD::NVV];
+  u32x4 kbuf[NRING][4][KL::NK], vbuf[NRING][4][KL::NV];
   float skb[NRING], svb[NRING];  // scales of the page this lane's scores belong to
   auto issue = [&](int k, int j) {
-    u32x4 (&kb)[4][GD::NKV] = kbuf[j];
-    u32x4 (&vb)[4][GD::NVV] = vbuf[j];
+    u32x4 (&kb)[4][KL::NK] = kbuf[j];
+    u32x4 (&vb)[4][KL::NV] = vbuf[j];
     float& skl = skb[j];
     float& svl = svb[j];
     if ((k & 15) == 0) load_batch(k);
@@ -827,17 +897,17 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
 #pragma unroll
     for (int pg = 0; pg < 4; ++pg) {
       const int32_t ph = __builtin_amdgcn_readlane(bt_v, e + pg);
-      const uint64_t base = chunk_offset(ph, h, p.num_kv_heads, D);
+      const uint64_t base = chunk_base<D, KF>(ph, h, p.num_kv_heads);
 #pragma unroll
-      for (int i = 0; i < GD::NKV; ++i)
+      for (int i = 0; i < KL::NK; ++i)
         kb[pg][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + base + koff[i]));
     }
 #pragma unroll
     for (int pg = 0; pg < 4; ++pg) {
       const int32_t ph = __builtin_amdgcn_readlane(bt_v, e + pg);
-      const uint64_t base = chunk_offset(ph, h, p.num_kv_heads, D);
+      const uint64_t base = chunk_base<D, KF>(ph, h, p.num_kv_heads);
 #pragma unroll
-      for (int i = 0; i < GD::NVV; ++i)
+      for (int i = 0; i < KL::NV; ++i)
         vb[pg][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + base + voff[i]));
     }
     skl = __shfl(sk_v, e + pj);
@@ -845,8 +915,8 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
   };
 
   auto step = [&](int k, int j) {
-    const u32x4 (&kc)[4][GD::NKV] = kbuf[j];
-    const u32x4 (&vc)[4][GD::NVV] = vbuf[j];
+    const u32x4 (&kc)[4][KL::NK] = kbuf[j];
+    const u32x4 (&vc)[4][KL::NV] = vbuf[j];
     const float skl = skb[j];
     const float svl = svb[j];
     const int c = c_begin + 2 * k;
@@ -858,8 +928,7 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < GD::NSLAB; ++s) {
-        const u32x4 w = kc[pg][(2 * s) / 4];
-        const bf16x8 kb = kv8x8_to_bf16x8<KI8>(w[(2 * s) % 4], w[(2 * s) % 4 + 1]);
+        const bf16x8 kb = k_slab<D, KF>(kc[pg], s);
 #pragma unroll
         for (int part = 0; part < NP; ++part)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[part][s], acc, 0, 0, 0);
@@ -916,15 +985,15 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
         vm1 = 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          vm0 |= (kc0 + j < L) ? (0xffu << (8 * j)) : 0u;
-          vm1 |= (kc0 + 16 + j < L) ? (0xffu << (8 * j)) : 0u;
+          vm0 |= (kc0 + j < L) ? slot_bits<KF>(j) : 0u;
+          vm1 |= (kc0 + 16 + j < L) ? slot_bits<KF>(j) : 0u;
         }
       }
 #pragma unroll
       for (int cblk = 0; cblk < GD::NVB; ++cblk) {
-        const uint32_t w0 = vc[2 * ch][cblk / 4][cblk % 4] & vm0;
-        const uint32_t w1 = vc[2 * ch + 1][cblk / 4][cblk % 4] & vm1;
-        const bf16x8 va = kv8x8_to_bf16x8<KI8>(w0, w1);
+        const uint32_t w0 = v_word<D, KF>(vc[2 * ch], cblk) & vm0;
+        const uint32_t w1 = v_word<D, KF>(vc[2 * ch + 1], cblk) & vm1;
+        const bf16x8 va = v8_to_bf16<KF>(w0, w1);
         o[cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bhi, o[cblk], 0, 0, 0);
         o[cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, blo, o[cblk], 0, 0, 0);
       }
@@ -1009,14 +1078,17 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
 // read by consecutive lanes.  Raw chunks wait in a ring of R register
 // buffers; LDS holds two converted chunks, so the one barrier per chunk both
 // publishes chunk k and frees the buffer of chunk k - 1 for chunk k + 1.
-template <int D, int NW>
+template <int D, int NW, int KF>
 struct TileGeo {
   using GD = Geo<D>;
-  static constexpr int NL = 2 * (GD::NKV + GD::NVV);  // 1 KB loads per chunk
-  static constexpr int LPT = NL / NW;                   // loads per thread per chunk
+  using KL = KvLoads<D, KF>;
+  static constexpr int NL = 2 * (KL::NK + KL::NV);     // 1 KB loads per chunk
+  // loads per thread per chunk; with fewer loads than waves (INT4 in eight
+  // waves) the last waves load nothing
+  static constexpr int LPT = (NL + NW - 1) / NW;
   static constexpr int KSL = 2 * GD::NSLAB;             // K operands: pages x slabs
   static constexpr int SLOTS = KSL + GD::NVB;           // + V operands: 16-row blocks of d
-  static_assert(NL % NW == 0, "the loads of a chunk split evenly over the waves");
+  static_assert(NL % NW == 0 || NL < NW, "the loads of a chunk split evenly over the loading waves");
 };
 
 __device__ __forceinline__ bf16x4 fp8x4_to_bf16x4(uint32_t w) {
@@ -1110,10 +1182,11 @@ __device__ __forceinline__ void load_q_operand(const StreamParams& p, size_t qof
   }
 }
 
-template <int D, int NW, int NT, bool QF32, bool OUTF32, int R, bool KI8, bool PP>
+template <int D, int NW, int NT, bool QF32, bool OUTF32, int R, int KF, bool PP>
 __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const PieceDesc& pc, int lane, int wave) {
   using GD = Geo<D>;
-  using TG = TileGeo<D, NW>;
+  using TG = TileGeo<D, NW, KF>;
+  using KL = KvLoads<D, KF>;
   constexpr int NP = QF32 ? 3 : 1;
   const int lq = lane >> 4;
   const int ln = lane & 15;
@@ -1157,22 +1230,22 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
   }
 
   // ---- this thread's share of a chunk's loads -----------------------------
-  // load r is slot j = r NW + wave of the chunk: K of page j / NKV, 16-byte
-  // block j % NKV of the lane's quarter of d (slabs 2 (j % NKV) and +1), or V
-  // of page j' / NVV (j' = j - 2 NKV), the lane's values d = NVB ln + 4 i ..
-  // +3 (i = j' % NVV) for the 4 keys of its quarter.
+  // load r is slot j = r NW + wave of the chunk (j < NL): K of page j / NK,
+  // 16-byte block j % NK of the lane's quarter of d, or V of page j' / NV
+  // (j' = j - 2 NK), the lane's values d = NVB ln + 4 i .. +3 (i = j' % NV)
+  // for the 4 keys of its quarter (INT4: all of its d-blocks, one load).
   uint32_t soff[TG::LPT];  // lane's byte offset inside the (page, head) chunk
   int ldpg[TG::LPT];
 #pragma unroll
   for (int r = 0; r < TG::LPT; ++r) {
     const int j = r * NW + wave;
-    if (j < 2 * GD::NKV) {
-      ldpg[r] = j / GD::NKV;
-      soff[r] = k_in_chunk(ln, lq * GD::DQ + 16 * (j % GD::NKV), D);
+    if (j < 2 * KL::NK) {
+      ldpg[r] = j / KL::NK;
+      soff[r] = k_lane_off<D, KF>(lq, ln, j % KL::NK);
     } else {
-      const int jj = j - 2 * GD::NKV;
-      ldpg[r] = jj / GD::NVV;
-      soff[r] = v_in_chunk(4 * lq, GD::NVB * ln + 4 * (jj % GD::NVV), D);
+      const int jj = j - 2 * KL::NK;
+      ldpg[r] = jj / KL::NV;
+      soff[r] = v_lane_off<D, KF>(lq, ln, jj % KL::NV);
     }
   }
 
@@ -1200,8 +1273,8 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
       const int pg = min(2 * (c_begin + k) + (lane & 1), npages - 1);  // a missing second page repeats the first
       ph = bt[pg];
       const int64_t sidx = (int64_t)ph * p.num_kv_heads + h;
-      a = p.kv_scales[sidx];
-      bsc = p.kv_scales[p.v_scale_offset + sidx];
+      a = p.kv_scales[sidx] * code_unit<KF>();
+      bsc = p.kv_scales[p.v_scale_offset + sidx] * code_unit<KF>();
     }
     bt_v = ph;
     sk_v = a * p.qk_scale_log2;
@@ -1221,10 +1294,11 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
     const int e = 2 * (k & 31);
 #pragma unroll
     for (int r = 0; r < TG::LPT; ++r) {
+      if (TG::NL % NW != 0 && r * NW + wave >= TG::NL) continue;  // wave-uniform
       const int32_t ph = __builtin_amdgcn_readlane(bt_v, e + ldpg[r]);
-      const uint8_t* pool = (r * NW + wave < 2 * GD::NKV) ? p.k_pages : p.v_pages;
+      const uint8_t* pool = (r * NW + wave < 2 * KL::NK) ? p.k_pages : p.v_pages;
       raw[j][r] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(pool + chunk_offset(ph, h, p.num_kv_heads, D) + soff[r]));
+          reinterpret_cast<const u32x4*>(pool + chunk_base<D, KF>(ph, h, p.num_kv_heads) + soff[r]));
     }
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
@@ -1241,25 +1315,41 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
     bf16x8 (*dst)[64] = s_kv[k % NB];
 #pragma unroll
     for (int r = 0; r < TG::LPT; ++r) {
-      const u32x4 w = raw[j][r];
       const int jj = r * NW + wave;
-      if (jj < 2 * GD::NKV) {
-        const int s0 = ldpg[r] * GD::NSLAB + 2 * (jj % GD::NKV);
-        dst[s0][lane] = kv8x8_to_bf16x8<KI8>(w[0], w[1]);
-        dst[s0 + 1][lane] = kv8x8_to_bf16x8<KI8>(w[2], w[3]);
+      if (TG::NL % NW != 0 && jj >= TG::NL) continue;  // wave-uniform
+      const u32x4 w = raw[j][r];
+      if (jj < 2 * KL::NK) {
+        if constexpr (KF == kKvInt4) {
+          // the lane's 32 codes of d: slabs 0..3 of its page
+#pragma unroll
+          for (int s2 = 0; s2 < GD::NSLAB; ++s2) dst[ldpg[r] * GD::NSLAB + s2][lane] = i4x8_to_bf16x8(w[s2]);
+        } else {
+          const int s0 = ldpg[r] * GD::NSLAB + 2 * (jj % KL::NK);
+          dst[s0][lane] = kv8x8_to_bf16x8<KF == kKvInt8>(w[0], w[1]);
+          dst[s0 + 1][lane] = kv8x8_to_bf16x8<KF == kKvInt8>(w[2], w[3]);
+        }
       } else {
-        // V bytes of keys >= L may be anything (NaN codes included): zero them
+        // V codes of keys >= L may be anything (NaN codes included): zero them
         const int key0 = c * kChunk + 16 * ldpg[r] + 4 * lq;
         uint32_t vm = 0xffffffffu;
         if (c * kChunk + kChunk > L) {
           vm = 0u;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vm |= (key0 + e < L) ? (0xffu << (8 * e)) : 0u;
+          for (int e = 0; e < 4; ++e) vm |= (key0 + e < L) ? slot_bits<KF>(e) : 0u;
         }
-        const int i = (jj - 2 * GD::NKV) % GD::NVV;
+        if constexpr (KF == kKvInt4) {
+          // four slots of every d-block of the lane's page
+          const u32x4 wv[1] = {w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          reinterpret_cast<bf16x4*>(&dst[TG::KSL + 4 * i + e][lane])[ldpg[r]] = kv8x4_to_bf16x4<KI8>(w[e] & vm);
+          for (int cb = 0; cb < GD::NVB; ++cb)
+            reinterpret_cast<bf16x4*>(&dst[TG::KSL + cb][lane])[ldpg[r]] = i4x4_to_bf16x4(v_word<D, KF>(wv, cb) & vm);
+        } else {
+          const int i = (jj - 2 * KL::NK) % KL::NV;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            reinterpret_cast<bf16x4*>(&dst[TG::KSL + 4 * i + e][lane])[ldpg[r]] =
+                kv8x4_to_bf16x4<KF == kKvInt8>(w[e] & vm);
+        }
       }
     }
     cm = rm[j];
@@ -1546,7 +1636,7 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
 // 4 waves take the chunks of a piece in turn (the workgroup is the unit).
 // Two waves per SIMD (256 registers each), one for the packed layout with
 // two groups in flight.
-template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int PR, bool KI8>
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int PR, int KF>
 __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
                              (NCT == 0 ? (PR == 1 ? 2 : 1) : 2)) void attn_stream_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
@@ -1562,9 +1652,9 @@ __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
   walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
     if constexpr (NCT == 0) {
       // at most 4 query columns: four pages per score tile
-      run_piece_packed<D, QF32, OUTF32, PR, KI8>(p, pc, lane);
+      run_piece_packed<D, QF32, OUTF32, PR, KF>(p, pc, lane);
     } else {
-      run_piece<D, NCT, DUPLO, QF32, OUTF32, 2, KI8>(p, pc, lane, wave);
+      run_piece<D, NCT, DUPLO, QF32, OUTF32, 2, KF>(p, pc, lane, wave);
     }
   });
 }
@@ -1590,7 +1680,7 @@ struct TileCfg {
   static constexpr bool PP = TILE_PINGPONG && NW == 8;
 };
 
-template <int D, int NW, int NT, bool QF32, bool OUTF32, bool KI8>
+template <int D, int NW, int NT, bool QF32, bool OUTF32, int KF>
 __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void attn_tile_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1603,7 +1693,7 @@ __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void at
   const int W = work_units(p, T);
   if (w >= W) return;
   walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
-    run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KI8, TileCfg<NW, NT>::PP>(p, pc, lane, wave);
+    run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KF, TileCfg<NW, NT>::PP>(p, pc, lane, wave);
   });
 }
 
@@ -1729,22 +1819,32 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(StreamParams
 
 template <int D, int NCT, bool DUPLO, int PR = 1>
 static const void* kernel_d(const Variant& v) {
-  // INT8 KV: bf16 Q and output only (the plan rejects the rest)
-  if (v.kv_int8) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR, true>);
+  // INT8 and INT4 KV: bf16 Q and output only (the plan rejects the rest)
+  if (v.kv_format == kKvInt8)
+    return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR, kKvInt8>);
+  if (v.kv_format == kKvInt4) {
+    if constexpr (D == 128)
+      return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR, kKvInt4>);
+    return nullptr;
+  }
   if (v.q_f32 && v.out_f32)
-    return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, true, PR, false>);
-  if (v.q_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, false, PR, false>);
-  if (v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, true, PR, false>);
-  return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR, false>);
+    return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, true, PR, kKvE4M3>);
+  if (v.q_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, true, false, PR, kKvE4M3>);
+  if (v.out_f32) return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, true, PR, kKvE4M3>);
+  return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR, kKvE4M3>);
 }
 
 template <int D, int NW, int NT>
 static const void* tile_d(const Variant& v) {
-  if (v.kv_int8) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, true>);
-  if (v.q_f32 && v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, true, false>);
-  if (v.q_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, false, false>);
-  if (v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, true, false>);
-  return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, false>);
+  if (v.kv_format == kKvInt8) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, kKvInt8>);
+  if (v.kv_format == kKvInt4) {
+    if constexpr (D == 128) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, kKvInt4>);
+    return nullptr;
+  }
+  if (v.q_f32 && v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, true, kKvE4M3>);
+  if (v.q_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, true, false, kKvE4M3>);
+  if (v.out_f32) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, true, kKvE4M3>);
+  return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, kKvE4M3>);
 }
 
 template <int D>

@@ -114,6 +114,69 @@ __device__ __forceinline__ bf16x4 kv8x4_to_bf16x4(uint32_t w) {
   }
 }
 
+// ---- KV formats (kKvE4M3, kKvInt8, kKvInt4: kernel_params.h) ----------------
+
+// Bytes of one (page, kv head) chunk: 16 slots x D codes.
+template <int KF>
+__host__ __device__ constexpr int chunk_bytes(int head_dim) {
+  return KF == kKvInt4 ? kPageSize * head_dim / 2 : kPageSize * head_dim;
+}
+
+// Byte offset of the (page, kv head) chunk in an INT4 pool.
+__device__ __forceinline__ uint64_t chunk_offset4(int32_t page, int head, int num_kv_heads, int head_dim) {
+  return ((uint64_t)(uint32_t)page * (uint64_t)num_kv_heads + (uint64_t)head) * (uint64_t)(kPageSize * head_dim / 2);
+}
+
+// INT4 chunks (D = 128): lane (lq, ln)'s 16 bytes start at (16 lq + ln) * 16
+// in both pools.  K: quarter lq of d of slot ln, codes d = 32 lq + u in byte
+// u / 2 (u even: low nibble).  V: the four slots 4 lq .. 4 lq + 3 of each
+// d = 8 ln + r in the 16-bit half r (slot 4 lq + j in nibble j).
+__device__ __forceinline__ uint32_t lane_in_chunk4(int lq, int ln) { return (uint32_t)((16 * lq + ln) * 16); }
+
+// K code (0..15) of (slot, d) in an INT4 chunk, and V code: for the gather hook.
+__device__ __forceinline__ uint32_t k4_code(const uint8_t* chunk, int slot, int d) {
+  const int u = d & 31;
+  return (chunk[lane_in_chunk4(d >> 5, slot) + (u >> 1)] >> (4 * (u & 1))) & 0xFu;
+}
+__device__ __forceinline__ uint32_t v4_code(const uint8_t* chunk, int slot, int d) {
+  const int a = d >> 3, r = d & 7;
+  return (chunk[lane_in_chunk4(slot >> 2, a) + 2 * r + ((slot & 3) >> 1)] >> (4 * (slot & 1))) & 0xFu;
+}
+
+__device__ __forceinline__ float sext_byte(uint32_t w, int e) { return (float)(int)(int8_t)(uint8_t)(w >> (8 * e)); }
+
+// Eight INT4 codes (w: code j in bits 4j..4j+3) -> eight bf16 holding 16
+// times their values, exactly: each code is moved to the top nibble of a
+// byte and sign-extended as an INT8 byte.  The caller's scales carry 1/16.
+__device__ __forceinline__ bf16x8 i4x8_to_bf16x8(uint32_t w) {
+  const uint32_t lo = (w << 4) & 0xF0F0F0F0u;  // codes 0, 2, 4, 6
+  const uint32_t hi = w & 0xF0F0F0F0u;         // codes 1, 3, 5, 7
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 pr = __builtin_convertvector(f32x2{sext_byte(lo, e), sext_byte(hi, e)}, bf16x2);
+    r[2 * e] = pr[0];
+    r[2 * e + 1] = pr[1];
+  }
+  return r;
+}
+
+// Four INT4 codes (h: code j in bits 4j..4j+3, j < 4) -> four bf16 of 16
+// times their values, exactly.
+__device__ __forceinline__ bf16x4 i4x4_to_bf16x4(uint32_t h) {
+  const uint32_t lo = (h << 4) & 0xF0F0u;  // codes 0, 2
+  const uint32_t hi = h & 0xF0F0u;         // codes 1, 3
+  const bf16x2 a = __builtin_convertvector(f32x2{sext_byte(lo, 0), sext_byte(hi, 0)}, bf16x2);
+  const bf16x2 b = __builtin_convertvector(f32x2{sext_byte(lo, 1), sext_byte(hi, 1)}, bf16x2);
+  return bf16x4{a[0], a[1], b[0], b[1]};
+}
+
+// The factor the decoded values carry: INT4 codes come out 16 times larger.
+template <int KF>
+__host__ __device__ constexpr float code_unit() {
+  return KF == kKvInt4 ? 0.0625f : 1.0f;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

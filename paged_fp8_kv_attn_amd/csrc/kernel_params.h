@@ -9,6 +9,12 @@ namespace pa {
 
 constexpr int kPageSize = 16;  // tokens per page
 
+// KV formats: OCP E4M3 bytes; INT8 bytes; INT4, two 4-bit two's-complement
+// codes per byte (low nibble first), head_dim 128 only.
+constexpr int kKvE4M3 = 0;
+constexpr int kKvInt8 = 1;
+constexpr int kKvInt4 = 2;
+
 struct StreamParams {
   const void* q;               // [sum Q][Hq][D] bf16 or fp32
   const uint8_t* k_pages;      // [P][Hkv][D/16][16][16]
@@ -48,7 +54,7 @@ struct Variant {
   bool dup_lo;      // low halves of P in spare columns (col_tiles == 1, <= 8 columns)
   bool q_f32;
   bool out_f32;
-  bool kv_int8;     // KV bytes are INT8 (two's complement) instead of OCP E4M3
+  int kv_format;    // 0: OCP E4M3 bytes; 1: INT8 bytes; 2: INT4, two codes per byte
 };
 
 constexpr int kWavesPerGroup = 4;
@@ -93,6 +99,7 @@ struct GatherParams {
   int32_t bt_stride;
   int32_t max_ctx_len;
   int64_t v_scale_offset;
+  int32_t kv_format;           // 2: INT4 pools (two codes per byte); otherwise one byte per value
 };
 
 // Paged FP8 KV append: the q_lens[b] new rows of each sequence become keys
@@ -141,6 +148,8 @@ hipError_t launch_debug_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_stream_read(const uint8_t* pool, int64_t pool_bytes, const int32_t* ids, int64_t num_chunks,
                               int32_t chunk_bytes, int32_t waves, uint32_t* sink, hipStream_t stream,
                               hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, bool kv_int8, hipStream_t stream);
+// kv_format 0/1: one E4M3/INT8 byte per value (n values); 2: n bytes of two
+// INT4 codes each (2n values, low nibble first).
+hipError_t launch_debug_decode(const uint8_t* in, float* out, int64_t n, int kv_format, hipStream_t stream);
 
 }  // namespace pa

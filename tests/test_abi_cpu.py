@@ -54,7 +54,9 @@ GOOD = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, num_pages=1
     (dict(sm_scale=-1.0), 1),
     (dict(q_dtype=7), 1),
     (dict(reserved=(0, 1, 0)), 1),
-    (dict(kv_format=2), 1),
+    (dict(kv_format=3), 1),
+    (dict(kv_format="int4", head_dim=64), 2),
+    (dict(kv_format="int4", q_dtype="f32"), 2),
     (dict(kv_format="int8", q_dtype="f32"), 2),
     (dict(kv_format="int8", out_dtype="f32"), 2),
     (dict(head_dim=96), 2),
