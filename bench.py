@@ -333,7 +333,9 @@ def stream_calibration(dev, args):
     library's attn_calib_stream_read; each repetition reads another slice of
     a random permutation of the pool's chunks, so no chunk is read twice in
     a row and the 256 MB Infinity Cache cannot hold what the next launch
-    reads.  Also a contiguous read of the same size (ids in order)."""
+    reads.  Also a contiguous read of the same size (ids in order), and the
+    2 KB random read with half of 16 lines per load instruction (the access
+    a plain [16 slots][128 bytes] page layout would give)."""
     import torch
 
     from paged_fp8_kv_attn_amd import calib_stream_read, load_library
@@ -351,14 +353,16 @@ def stream_calibration(dev, args):
         nchunks = target // chunk
         pool_chunks = pool_bytes // chunk
         perm = rng.permutation(pool_chunks).astype(np.int32)
-        for order in ("random", "sequential"):
+        for order in ("random", "sequential", "half_lines"):
             if order == "sequential" and chunk != 65536:
+                continue
+            if order == "half_lines" and chunk != 2048:
                 continue
             for waves in (1024, 2048, 4096):
                 sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
                 times = []
                 for r in range(reps + 1):
-                    if order == "random":
+                    if order != "sequential":
                         lo = (r * nchunks) % (pool_chunks - nchunks)
                         ids = torch.from_numpy(perm[lo:lo + nchunks].copy()).to(dev)
                     else:
@@ -366,7 +370,8 @@ def stream_calibration(dev, args):
                         ids = torch.arange(start, start + nchunks, dtype=torch.int32, device=dev)
                     a, b = hipt.event(), hipt.event()
                     torch.cuda.synchronize()
-                    calib_stream_read(pool, ids, chunk, waves, sink, kernel_events=(a, b))
+                    calib_stream_read(pool, ids, chunk, waves, sink, kernel_events=(a, b),
+                                      access=1 if order == "half_lines" else 0)
                     torch.cuda.synchronize()
                     if r > 0:  # the first launch is a warm-up
                         times.append(hipt.elapsed_ms(a, b))
@@ -388,10 +393,13 @@ def stream_calibration(dev, args):
                  "# launch, 16-byte non-temporal loads, 16 lines of 1 KB in flight per wave, waves streaming equal",
                  "# contiguous shares of the chunk list; the best of 1024/2048/4096 waves, median of "
                  f"{reps} launches",
-                 "# timed with HIP events attached to the kernel's dispatch.  'sequential' reads consecutive chunks.",
+                 "# timed with HIP events attached to the kernel's dispatch.  'sequential' reads consecutive chunks;",
+                 "# 'half_line' reads the 2 KB random chunks as 16 rows of 128 bytes, each load instruction touching",
+                 "# half of 16 lines (32 bytes of a row per lane in two 16-byte loads).",
                  "# command: python bench.py --stream-calibration --summary-out profiles/stream_read_ceiling.txt"]
         for (chunk, order), r in sorted(best.items()):
-            tag = "chunk_bytes" if order == "random" else "sequential_chunk_bytes"
+            tag = {"random": "chunk_bytes", "sequential": "sequential_chunk_bytes",
+                   "half_lines": "half_line_chunk_bytes"}[order]
             lines.append(f"{tag}={chunk} best_GBps={r['GBps']:.1f} waves={r['waves']} median_us={r['median_us']:.2f} "
                          f"bytes={r['bytes']}")
         lines.append("# all runs:")

@@ -345,6 +345,13 @@ attn_status_t attn_debug_encode_fp8(const float* in, uint8_t* out, int64_t n, hi
  * loads, `waves` waves each streaming an equal contiguous share of the list,
  * and writes one XOR word per lane to sink (waves * 64 uint32, so the loads
  * cannot be dropped).  No other arithmetic.
+ *   access      0: the 64 lanes of a wave read 1 KB of whole 128-byte lines
+ *               per instruction (the pattern of this library's page
+ *               layouts); 1 (chunk_bytes >= 2048): each 2 KB is 16 rows of
+ *               128 bytes, lane (q, r) (q = lane / 16, r = lane % 16) reads
+ *               bytes 32 q + 16 i of row r in instruction i = 0, 1 -- half
+ *               of 16 lines per instruction, the pattern of a [16 slots][128]
+ *               byte layout read as 32 values of d per lane
  *   pool        device memory of pool_bytes (>= chunk_bytes), 16-byte aligned;
  *               ids outside [0, pool_bytes / chunk_bytes) are clamped into it
  *   chunk_ids   int32 [num_chunks], device memory
@@ -355,8 +362,9 @@ attn_status_t attn_debug_encode_fp8(const float* in, uint8_t* out, int64_t n, hi
  * Asynchronous on `stream`; allocates nothing.  Not part of the attention
  * path. */
 attn_status_t attn_calib_stream_read(const uint8_t* pool, int64_t pool_bytes, const int32_t* chunk_ids,
-                                     int64_t num_chunks, int32_t chunk_bytes, int32_t waves, uint32_t* sink,
-                                     hipEvent_t kernel_start, hipEvent_t kernel_stop, hipStream_t stream);
+                                     int64_t num_chunks, int32_t chunk_bytes, int32_t waves, int32_t access,
+                                     uint32_t* sink, hipEvent_t kernel_start, hipEvent_t kernel_stop,
+                                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -142,7 +142,7 @@ def load_library():
     lib.attn_mtp_accept_workspace_size.restype = ctypes.c_size_t
     lib.attn_mtp_accept.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp, vp, vp]
     lib.attn_mtp_accept.restype = i32
-    lib.attn_calib_stream_read.argtypes = [vp, i64, vp, i64, i32, i32, vp, vp, vp, vp]
+    lib.attn_calib_stream_read.argtypes = [vp, i64, vp, i64, i32, i32, i32, vp, vp, vp, vp]
     lib.attn_calib_stream_read.restype = i32
     lib.attn_paged_forward_static.argtypes = [ctypes.POINTER(PlanDesc)] + [vp] * 9
     lib.attn_paged_forward_static.restype = i32
@@ -465,7 +465,8 @@ def mtp_accept(logits, drafts, target_tokens, num_accepted, workspace, kernel_ev
     _check(st, "attn_mtp_accept")
 
 
-def calib_stream_read(pool, chunk_ids, chunk_bytes: int, waves: int, sink, kernel_events=None, stream=None):
+def calib_stream_read(pool, chunk_ids, chunk_bytes: int, waves: int, sink, kernel_events=None, stream=None,
+                      access: int = 0):
     """Streaming-read calibration (attn_calib_stream_read): `waves` waves read
     the chunks chunk_ids (int32 device tensor) of chunk_bytes each from pool
     (uint8 device tensor) and write one XOR word per lane into sink (int32 or
@@ -477,5 +478,5 @@ def calib_stream_read(pool, chunk_ids, chunk_bytes: int, waves: int, sink, kerne
                                                         for e in kernel_events)
     st = load_library().attn_calib_stream_read(
         _ptr(pool), pool.numel() * pool.element_size(), _ptr(chunk_ids), int(chunk_ids.numel()), int(chunk_bytes),
-        int(waves), _ptr(sink), ev[0], ev[1], _stream(stream))
+        int(waves), int(access), _ptr(sink), ev[0], ev[1], _stream(stream))
     _check(st, "attn_calib_stream_read")

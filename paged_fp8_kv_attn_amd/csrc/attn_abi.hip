@@ -571,18 +571,20 @@ attn_status_t attn_mtp_accept(const void* logits, attn_dtype_t logits_dtype, con
 }
 
 attn_status_t attn_calib_stream_read(const uint8_t* pool, int64_t pool_bytes, const int32_t* chunk_ids,
-                                     int64_t num_chunks, int32_t chunk_bytes, int32_t waves, uint32_t* sink,
-                                     hipEvent_t kernel_start, hipEvent_t kernel_stop, hipStream_t stream) {
+                                     int64_t num_chunks, int32_t chunk_bytes, int32_t waves, int32_t access,
+                                     uint32_t* sink, hipEvent_t kernel_start, hipEvent_t kernel_stop,
+                                     hipStream_t stream) {
   if (!pool || !chunk_ids || !sink) return ATTN_ERR_INVALID_ARGUMENT;
   if (chunk_bytes < 1024 || chunk_bytes > (1 << 24) || (chunk_bytes & (chunk_bytes - 1)) != 0)
     return ATTN_ERR_INVALID_ARGUMENT;
   if (pool_bytes < chunk_bytes || num_chunks < 1 || num_chunks > (int64_t{1} << 40) / chunk_bytes)
     return ATTN_ERR_INVALID_ARGUMENT;
   if (waves < 1 || waves > (1 << 20)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (access != 0 && (access != 1 || chunk_bytes < 2048)) return ATTN_ERR_INVALID_ARGUMENT;
   if ((kernel_start == nullptr) != (kernel_stop == nullptr)) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned(pool, 16) || !aligned(chunk_ids, 4) || !aligned(sink, 4)) return ATTN_ERR_INVALID_ARGUMENT;
-  const hipError_t e = pa::launch_stream_read(pool, pool_bytes, chunk_ids, num_chunks, chunk_bytes, waves, sink,
-                                              stream, kernel_start, kernel_stop);
+  const hipError_t e = pa::launch_stream_read(pool, pool_bytes, chunk_ids, num_chunks, chunk_bytes, waves, access,
+                                              sink, stream, kernel_start, kernel_stop);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

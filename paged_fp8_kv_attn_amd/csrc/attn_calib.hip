@@ -6,8 +6,13 @@
 //
 // Wave w of W streams the 1 KB lines [floor(w N / W), floor((w+1) N / W))
 // of the N lines the chunks hold, in list order, with 16-byte non-temporal
-// loads (64 lanes read one whole 1 KB line per instruction) kept NR deep in
-// a ring of registers.
+// loads kept NR deep in a ring of registers.  Access 0: the 64 lanes read
+// one whole 1 KB run per instruction (eight whole 128-byte lines), the
+// pattern of the library's page layouts.  Access 1: each 2 KB of a chunk is
+// 16 rows of 128 bytes and lane (q, r) of a wave (q = lane / 16, r = lane %
+// 16) reads bytes 32 q + 16 i of row r in instruction i = 0, 1, so every
+// instruction touches half of 16 lines: the pattern a [16 slots][128 d]
+// page layout gives a lane that holds 32 values of d of one slot.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -30,6 +35,7 @@ struct CalibParams {
   int64_t num_lines;    // chunks * lines_per_chunk
   int32_t lpc_log2;     // log2(chunk_bytes / 1024)
   int32_t waves;
+  int32_t access;       // 0: whole lines per instruction; 1: half lines
   uint32_t* sink;       // [waves * 64]
 };
 
@@ -43,7 +49,11 @@ __global__ __launch_bounds__(64 * kCalibWaves) void stream_read_kernel(CalibPara
     const int64_t c = line >> p.lpc_log2;
     int64_t id = p.ids[c];
     id = id < 0 ? 0 : (id >= p.pool_chunks ? p.pool_chunks - 1 : id);
-    const int64_t off = ((id << p.lpc_log2) + (line & ((1 << p.lpc_log2) - 1))) * 1024 + lane * 16;
+    const int64_t li = line & ((1 << p.lpc_log2) - 1);  // 1 KB line inside the chunk
+    const int64_t lane_off = p.access == 0 ? lane * 16
+                                           : (li & ~int64_t{1}) * 1024 + (lane & 15) * 128 + (lane >> 4) * 32 +
+                                                 (li & 1) * 16 - li * 1024;
+    const int64_t off = ((id << p.lpc_log2) + li) * 1024 + lane_off;
     return reinterpret_cast<const u32x4*>(p.pool + off);
   };
   u32x4 acc = {0u, 0u, 0u, 0u};
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(64 * kCalibWaves) void stream_read_kernel(CalibPara
 }  // namespace
 
 hipError_t launch_stream_read(const uint8_t* pool, int64_t pool_bytes, const int32_t* ids, int64_t num_chunks,
-                              int32_t chunk_bytes, int32_t waves, uint32_t* sink, hipStream_t stream,
+                              int32_t chunk_bytes, int32_t waves, int32_t access, uint32_t* sink, hipStream_t stream,
                               hipEvent_t ev_start, hipEvent_t ev_stop) {
   int lpc_log2 = 0;
   while ((1024 << lpc_log2) < chunk_bytes) ++lpc_log2;
@@ -89,6 +99,7 @@ hipError_t launch_stream_read(const uint8_t* pool, int64_t pool_bytes, const int
   p.num_lines = num_chunks << lpc_log2;
   p.lpc_log2 = lpc_log2;
   p.waves = waves;
+  p.access = access;
   p.sink = sink;
   const int grid = (waves + kCalibWaves - 1) / kCalibWaves;
   void* args[] = {&p};

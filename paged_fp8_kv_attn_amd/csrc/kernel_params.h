@@ -144,9 +144,10 @@ hipError_t launch_mtp_accept(const AcceptParams& p, bool f32, hipStream_t stream
 hipError_t launch_debug_gather(const GatherParams& p, hipStream_t stream);
 // Streaming-read calibration: `waves` waves read the chunk_bytes-sized chunks
 // ids[0..num_chunks) of pool (ids clamped to the pool) and write one XOR word
-// per lane to sink[waves * 64].  chunk_bytes: a power of two >= 1024.
+// per lane to sink[waves * 64].  chunk_bytes: a power of two >= 1024 (>= 2048
+// with access 1: half lines of 16 rows of 128 bytes per instruction).
 hipError_t launch_stream_read(const uint8_t* pool, int64_t pool_bytes, const int32_t* ids, int64_t num_chunks,
-                              int32_t chunk_bytes, int32_t waves, uint32_t* sink, hipStream_t stream,
+                              int32_t chunk_bytes, int32_t waves, int32_t access, uint32_t* sink, hipStream_t stream,
                               hipEvent_t ev_start, hipEvent_t ev_stop);
 // kv_format 0/1: one E4M3/INT8 byte per value (n values); 2: n bytes of two
 // INT4 codes each (2n values, low nibble first).

@@ -91,3 +91,18 @@ def test_null_arguments_rejected():
     assert lib.attn_mtp_accept(None, 1, None, 1, 4, 64, None, None, None, 0, None, None, None) == 1
     assert lib.attn_mtp_accept_workspace_size(0, 4, 64) == 0
     assert lib.attn_mtp_accept_workspace_size(128, 4, 151936) > 0
+
+
+@pytest.mark.parametrize("chunk_bytes,waves,access", [
+    (1024, 64, 1),      # half-line access needs 2 KB rows of 16 x 128 bytes
+    (2048, 64, 2),      # no such access pattern
+    (3072, 64, 0),      # not a power of two
+    (512, 64, 0),       # below one 1 KB line
+    (2048, 0, 0),       # no waves
+])
+def test_calibration_arguments_rejected(chunk_bytes, waves, access):
+    import ctypes as c
+    lib = pa.load_library()
+    fake = c.c_void_p(1 << 20)  # aligned, non-null, never dereferenced: rejected first
+    assert lib.attn_calib_stream_read(fake, 1 << 30, fake, 16, chunk_bytes, waves, access, fake,
+                                      None, None, None) == 1
