@@ -63,6 +63,11 @@
 #ifndef TILE_PP_PARITY
 #define TILE_PP_PARITY 0
 #endif
+// Wave priority in the tile kernel: 1 raises it while a wave issues its
+// matrix products, 2 while it runs the softmax, 0 leaves it.
+#ifndef TILE_SETPRIO
+#define TILE_SETPRIO 1
+#endif
 
 namespace pa {
 
@@ -1357,6 +1362,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
 
   // S^T = K Q^T for both pages of chunk k
   auto qk = [&](int k, f32x4 (&sacc)[2][NT]) {
+    if (TILE_SETPRIO == 1) __builtin_amdgcn_s_setprio(1);
     const bf16x8 (*kv)[64] = s_kv[k % NB];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
@@ -1372,6 +1378,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
             sacc[pg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[t][part][s], sacc[pg][t], 0, 0, 0);
       }
     }
+    if (TILE_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
   };
 
   // Online softmax of one chunk in log2 units with a lazy running max: the
@@ -1383,6 +1390,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
   // hi + lo operands.
   auto softmax = [&](int k, const ChunkMeta& ch, f32x4 (&sacc)[2][NT], bf16x8 (&pop_hi)[NT],
                      bf16x8 (&pop_lo)[NT]) {
+    if (TILE_SETPRIO == 2) __builtin_amdgcn_s_setprio(1);
     const int cu = __builtin_amdgcn_readfirstlane(c_begin + k);
     const int key0 = cu * kChunk + 4 * lq;  // key of register j: key0 + j (page 0), key0 + 16 + j (page 1)
     const bool need_mask = (cu * kChunk + kChunk - 1) >= first_masked_key;
@@ -1436,10 +1444,12 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
       pop_hi[t] = __builtin_bit_cast(bf16x8, u32x4{phi[0], phi[1], phi[2], phi[3]});
       pop_lo[t] = __builtin_bit_cast(bf16x8, u32x4{plo[0], plo[1], plo[2], plo[3]});
     }
+    if (TILE_SETPRIO == 2) __builtin_amdgcn_s_setprio(0);
   };
 
   // O^T += V^T P~^T for chunk k
   auto pv = [&](int k, const bf16x8 (&pop_hi)[NT], const bf16x8 (&pop_lo)[NT]) {
+    if (TILE_SETPRIO == 1) __builtin_amdgcn_s_setprio(1);
     const bf16x8 (*kv)[64] = s_kv[k % NB];
 #pragma unroll
     for (int cblk = 0; cblk < GD::NVB; ++cblk) {
@@ -1450,6 +1460,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
         o[t][cblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[t], o[t][cblk], 0, 0, 0);
       }
     }
+    if (TILE_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
   };
 
   // Ping-pong (PP): the waves of the first half (one per SIMD) issue their
@@ -1604,6 +1615,17 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
     pc.whole = (r == 0) && (take == n);
     const int seg = (b * p.num_kv_heads + h) * p.col_blocks + cb;
     pc.slot = seg + w;
+    // the same in every lane: hand the piece over in scalar registers
+    pc.b = __builtin_amdgcn_readfirstlane(pc.b);
+    pc.h = __builtin_amdgcn_readfirstlane(pc.h);
+    pc.cb = __builtin_amdgcn_readfirstlane(pc.cb);
+    pc.L = __builtin_amdgcn_readfirstlane(pc.L);
+    pc.Q = __builtin_amdgcn_readfirstlane(pc.Q);
+    pc.row0 = __builtin_amdgcn_readfirstlane(pc.row0);
+    pc.c_begin = __builtin_amdgcn_readfirstlane(pc.c_begin);
+    pc.c_end = __builtin_amdgcn_readfirstlane(pc.c_end);
+    pc.whole = __builtin_amdgcn_readfirstlane((int)pc.whole) != 0;
+    pc.slot = __builtin_amdgcn_readfirstlane(pc.slot);
     if (r == 0 && leader) {
       // units w .. last hold the pieces; their partial slots are seg + w ..
       const int last = pc.whole ? w : wg_of_chunk(cur + n - 1, T, W);
