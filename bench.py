@@ -747,7 +747,9 @@ def main():
     # a sleep kernel does the same).
     hipt = HipGraph()
     ev = [([hipt.event() for _ in range(args.steps)], [hipt.event() for _ in range(args.steps)]) for _ in parts]
-    has_merge = [hasattr(pt.plan, "set_merge_events") for pt in parts]
+    # the attention forward launches a merge kernel; the append and the
+    # acceptance do not (their events would never be recorded)
+    has_merge = [isinstance(pt, Part) for pt in parts]
     mev = [([hipt.event() for _ in range(args.steps)], [hipt.event() for _ in range(args.steps)]) if hm else None
            for hm in has_merge]
     torch.cuda.synchronize()
