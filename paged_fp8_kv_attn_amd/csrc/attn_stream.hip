@@ -949,11 +949,14 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = (kl + i <= lim && kl + i < kend) ? x[i] : kNegInf;
     }
+    // the lane's max; a column's max passes m + 8 iff one of its lanes'
+    // does, so the reduction over the column's 16 lanes runs only when the
+    // reference moves
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = max_over_lq(mx);
-    mx = fmaxf(mx, dpp_ror4(mx));
-    mx = fmaxf(mx, dpp_ror8(mx));
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazyLog2)) {
+      mx = max_over_lq(mx);
+      mx = fmaxf(mx, dpp_ror4(mx));
+      mx = fmaxf(mx, dpp_ror8(mx));
       const float mn = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - ((mn == kNegInf) ? 0.f : mn));
 #pragma unroll
@@ -1407,14 +1410,15 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
                                                      __builtin_elementwise_maximum(sacc[0][t][2], sacc[0][t][3]));
       const float r1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[1][t][0], sacc[1][t][1]),
                                                      __builtin_elementwise_maximum(sacc[1][t][2], sacc[1][t][3]));
+      // the lane's max over its 8 keys; some column's max passes m + 8 iff
+      // some lane's does, so the reduction across the column's four lanes
+      // runs only when the reference moves
       float mx = __builtin_elementwise_maximum(r0 * ch.fk[0], r1 * ch.fk[1]);
-      {
+      if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyLog2)) {
         auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
         auto c2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = __builtin_elementwise_maximum(__uint_as_float(c2[0]), __uint_as_float(c2[1]));
-      }
-      if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyLog2)) {
         const float mn = fmaxf(m[t], mx);
         const float alpha = __builtin_amdgcn_exp2f(m[t] - ((mn == kNegInf) ? 0.f : mn));
 #pragma unroll
