@@ -3,6 +3,7 @@ bytes times the page scale) with the fp64 oracle, through the C ABI: every
 kernel family (packed decode, single tile, shared-KV tile), forced
 partitions, ragged tails, D 64 and 128."""
 
+import numpy as np
 import pytest
 
 from synth import custom_workload, make_workload
@@ -13,14 +14,16 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-def _parity(w, **over):
+def _parity(w, rows=None, **over):
     log(f"int8 parity: {w.name} seed={w.seed} B={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"D={w.head_dim} q_lens={sorted(set(w.q_lens.tolist()))[:4]} ctx=[{w.ctx_lens.min()},{w.ctx_lens.max()}]")
     plan = plan_for(w, kv_format="int8", **over)
     got = run_gpu(w, plan=plan)
     plan.close()
     ref = oracle.paged_attention(w.q, w.k_pages, w.v_pages, w.kv_scales, w.block_table, w.ctx_lens, w.q_lens,
-                                 num_kv_heads=w.num_kv_heads, sm_scale=w.sm_scale, kv_format="int8")
+                                 num_kv_heads=w.num_kv_heads, sm_scale=w.sm_scale, kv_format="int8", rows=rows)
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
     return check_contract(got, ref, w.out_dtype, what=f"int8 {w.name}")
 
 
@@ -40,6 +43,23 @@ def test_int8_reduced(name):
 
 def test_int8_llama3_full():
     _parity(make_workload("llama3_8b_decode", kv_format="int8", keep_logical=False))
+
+
+@pytest.mark.parametrize("name", ["mtp_verify", "mqa_decode", "long_ctx_split"])
+def test_int8_full(name):
+    w = make_workload(name, kv_format="int8", keep_logical=False)
+    stats = _parity(w)
+    assert stats["n"] == w.total_q * w.num_q_heads * w.head_dim
+
+
+def test_int8_prefill_full_sampled_rows():
+    # every sequence's first, page-edge and last new tokens, plus random rows
+    w = make_workload("prefill_chunk", kv_format="int8", keep_logical=False)
+    rng = np.random.default_rng(1)
+    starts = np.concatenate([[0], np.cumsum(w.q_lens)[:-1]])
+    rows = sorted(set(int(s + i) for s in starts for i in [0, 15, 16, 255, 511])
+                  | set(rng.integers(0, w.total_q, 48).tolist()))
+    _parity(w, rows=rows)
 
 
 EDGE = [

@@ -65,7 +65,7 @@ def test_prefill_chunk_full_sampled_rows():
     rng = np.random.default_rng(0)
     starts = np.concatenate([[0], np.cumsum(w.q_lens)[:-1]])
     rows = sorted(set(int(s + i) for s in starts for i in [0, 1, 2, 15, 16, 17, 63, 64, 255, 256, 510, 511])
-                  | set(rng.integers(0, w.total_q, 64).tolist()))
+                  | set(rng.integers(0, w.total_q, 256).tolist()))
     _parity(w, rows=rows)
 
 
