@@ -79,6 +79,8 @@ constexpr int kMinChunksPerWave = 8;    // a wave's share in the packed layout
 #define TILE_MIN_CHUNKS 16
 #endif
 constexpr int kMinChunksPerTile = TILE_MIN_CHUNKS;
+constexpr int kStartCostPacked = 1;  // chunks a segment start counts for (see choose_plan)
+constexpr int kStartCostTile = 3;
 
 attn_status_t validate_desc(const attn_plan_desc_t& d) {
   for (int r : d.reserved)
@@ -216,10 +218,11 @@ attn_status_t choose_plan(const attn_plan_desc_t& d, int device, attn_plan_s* p)
   // which a quarter of the waves do so ran 31.6-32.3 us against 30.0-30.2 us
   // for the same bytes with none.  The balanced split counts each segment
   // start as chunks, so those units stream that much less: one for the
-  // packed decode, two for the tile kernel, whose restart also refills its
-  // ring and LDS staging (measured best of 0-2 on each).  A forced split
-  // count keeps its exact cut: n equal pieces of every segment.
-  p->start_cost = d.num_kv_splits != 0 ? 0 : (v.packed ? 1 : 2);
+  // packed decode (3 and 5 measured no better), three for the tile kernels,
+  // whose restart also refills the ring and LDS staging (the prefill chunk
+  // 420 us with 3 or 4 against 432 us with 2; MQA and MTP unchanged).  A
+  // forced split count keeps its exact cut: n equal pieces of every segment.
+  p->start_cost = d.num_kv_splits != 0 ? 0 : (v.packed ? kStartCostPacked : kStartCostTile);
   p->grid = static_cast<int>(ceil_div(units * unit_waves, wpg));
   // merge: one workgroup per segment (and slice of its columns); segments
   // with many pieces on average get fewer columns per workgroup

@@ -262,19 +262,20 @@ struct SeqStart {
   int L, Q;
 };
 
-// Total chunks over all sequences (wave-uniform); `c0` holds the first 64.
-__device__ int64_t total_chunks(const StreamParams& p, int lane, const SeqLens& c0) {
-  int64_t total = wave_sum64(c0.nb);
-  for (int base = 64; base < p.num_seqs; base += 64) total += wave_sum64(load_seq(p, base + lane).nb);
+// Total chunks over all sequences (wave-uniform); `c0` and `c1` hold
+// sequences 0 .. 63 and 64 .. 127 (loaded together at the kernel's start).
+__device__ int64_t total_chunks(const StreamParams& p, int lane, const SeqLens& c0, const SeqLens& c1) {
+  int64_t total = wave_sum64(c0.nb) + wave_sum64(c1.nb);
+  for (int base = 128; base < p.num_seqs; base += 64) total += wave_sum64(load_seq(p, base + lane).nb);
   return total;
 }
 
 // The sequence whose chunks contain global chunk `pos` (< total).
-__device__ SeqStart locate_seq(const StreamParams& p, int64_t pos, int lane, const SeqLens& c0) {
+__device__ SeqStart locate_seq(const StreamParams& p, int64_t pos, int lane, const SeqLens& c0, const SeqLens& c1) {
   int64_t carry = 0;
   int rows = 0;
   for (int base = 0; base < p.num_seqs; base += 64) {
-    const SeqLens c = (base == 0) ? c0 : load_seq(p, base + lane);
+    const SeqLens c = (base == 0) ? c0 : (base == 64) ? c1 : load_seq(p, base + lane);
     const int64_t incl = wave_incl_scan64(c.nb, lane);
     const int qincl = (int)wave_incl_scan64(c.Q, lane);
     const int64_t start = carry + incl - c.nb;
@@ -1581,11 +1582,11 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
 // many units hold pieces of it (1: written whole).
 template <class Run>
 __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, bool leader, int w, int W, int64_t T,
-                                            const SeqLens& c0, Run&& run) {
+                                            const SeqLens& c0, const SeqLens& c1, Run&& run) {
   const int64_t lo = (int64_t)w * T / W;
   const int64_t hi = (int64_t)(w + 1) * T / W;
   if (lo >= hi) return;
-  SeqStart ss = locate_seq(p, lo, lane, c0);
+  SeqStart ss = locate_seq(p, lo, lane, c0, c1);
   int b = ss.b;
   int row0 = ss.row0;
   int L = ss.L;
@@ -1672,10 +1673,11 @@ __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
 
   if (blockIdx.x == 0 && wave == 0) write_seq_meta(p, lane);
   const SeqLens c0 = load_seq(p, lane);
-  const int64_t T = total_chunks(p, lane, c0);
+  const SeqLens c1 = load_seq(p, 64 + lane);
+  const int64_t T = total_chunks(p, lane, c0, c1);
   const int W = work_units(p, T);
   if (w >= W) return;
-  walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
+  walk_pieces(p, lane, leader, w, W, T, c0, c1, [&](const PieceDesc& pc) {
     if constexpr (NCT == 0) {
       // at most 4 query columns: four pages per score tile
       run_piece_packed<D, QF32, OUTF32, PR, KF>(p, pc, lane);
@@ -1715,10 +1717,11 @@ __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void at
 
   if (w == 0 && wave == 0) write_seq_meta(p, lane);
   const SeqLens c0 = load_seq(p, lane);
-  const int64_t T = total_chunks(p, lane, c0);
+  const SeqLens c1 = load_seq(p, 64 + lane);
+  const int64_t T = total_chunks(p, lane, c0, c1);
   const int W = work_units(p, T);
   if (w >= W) return;
-  walk_pieces(p, lane, leader, w, W, T, c0, [&](const PieceDesc& pc) {
+  walk_pieces(p, lane, leader, w, W, T, c0, c1, [&](const PieceDesc& pc) {
     run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KF, TileCfg<NW, NT>::PP>(p, pc, lane, wave);
   });
 }

@@ -77,7 +77,7 @@ def _check(real, w_max, min_chunks, start_cost):
         assert any(ce > cb for _, cb, ce, _ in ps)  # some unit reads the segment
 
 
-@pytest.mark.parametrize("start_cost", [0, 1, 2])
+@pytest.mark.parametrize("start_cost", [0, 1, 2, 3])
 def test_schedule_random_mixes(start_cost):
     rng = random.Random(100 + start_cost)
     for _ in range(600):
