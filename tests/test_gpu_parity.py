@@ -98,6 +98,33 @@ def test_edge_cases(idx):
     _parity(w)
 
 
+# Batches beyond 128 sequences: the kernels hold the lengths of sequences
+# 0..127 in lanes and read the others from memory while they count chunks,
+# locate a unit's first sequence and step to the next one; the merge needs
+# every sequence's first query row.
+MANY = [
+    # (B, q_len, ctx range, Hq, Hkv, forced splits): kernel family exercised
+    (300, 1, (1, 300), 8, 2, 0),     # packed decode, short and split sequences
+    (300, 1, (1, 300), 8, 2, 3),     # packed decode, forced partitions beyond one resident round
+    (260, 2, (2, 200), 8, 2, 0),     # single tile with the low halves of P in spare columns (8 columns)
+    (260, 2, (2, 200), 16, 2, 0),    # single tile (16 columns)
+    (150, 5, (5, 400), 40, 8, 0),    # shared-KV tile, two waves (25 columns)
+    (200, 1, (1, 600), 64, 1, 0),    # shared-KV tile, four waves (64 columns)
+    (140, 16, (16, 300), 32, 2, 0),  # shared-KV tile, eight waves (256-column blocks)
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MANY)))
+def test_many_sequences(idx):
+    B, ql, (lo, hi), hq, hkv, splits = MANY[idx]
+    rng = np.random.default_rng(700 + idx)
+    ctx = rng.integers(max(lo, ql), hi + 1, size=B).tolist()
+    w = custom_workload([ql] * B, ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, seed=700 + idx,
+                        num_kv_splits=splits, name=f"many{idx}")
+    assert w.num_seqs > 128
+    _parity(w)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
 def test_forced_partitions(splits):
     w = custom_workload([1, 1, 1], [1000, 37, 2048], num_q_heads=8, num_kv_heads=2, head_dim=128, seed=200,
