@@ -33,6 +33,7 @@ struct attn_plan_s {
   int max_units;     // waves (packed) or workgroups sharing the key chunks
   int unit_min_chunks;  // chunks per unit at least (within [1, max_units] units)
   int start_cost;       // chunks a segment's start counts for in the balanced split
+  bool whole_ok;        // the tile kernel may give each unit one segment whole
   int occupancy;     // resident attention workgroups per compute unit
   int num_cus;
   float sm_scale;
@@ -223,6 +224,14 @@ attn_status_t choose_plan(const attn_plan_desc_t& d, int device, attn_plan_s* p)
   // 420 us with 3 or 4 against 432 us with 2; MQA and MTP unchanged).  A
   // forced split count keeps its exact cut: n equal pieces of every segment.
   p->start_cost = d.num_kv_splits != 0 ? 0 : (v.packed ? kStartCostPacked : kStartCostTile);
+  // Where the segments are about as many as the units and of similar
+  // lengths, the shared-KV tile kernel gives each unit one segment whole
+  // (it decides from the lengths of each forward): the MTP verification
+  // shape (1024 segments of 4-36 chunks) then ran 54.9-55.3 us per step
+  // against 58.8-59.0 us for the balanced split (kernel 50.3-50.4 against
+  // 48.6-49.0 us; the merge finds nothing to do).  Not with a forced split
+  // count.
+  p->whole_ok = d.num_kv_splits == 0 && v.tile_waves > 0;
   p->grid = static_cast<int>(ceil_div(units * unit_waves, wpg));
   // merge: one workgroup per segment (and slice of its columns); segments
   // with many pieces on average get fewer columns per workgroup
@@ -295,6 +304,7 @@ attn_status_t enqueue_forward(const attn_plan_s* plan, const void* q, const uint
   sp.unit_min_chunks = plan->unit_min_chunks;
   sp.max_units = plan->max_units;
   sp.start_cost = plan->start_cost;
+  sp.whole_ok = plan->whole_ok ? 1 : 0;
   sp.seq_row0 = plan->seq_row0;
   sp.seg_merge = plan->seg_merge;
   sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;

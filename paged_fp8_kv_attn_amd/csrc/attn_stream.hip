@@ -1657,6 +1657,74 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
   }
 }
 
+// Whole-segment schedule of the shared-KV tile kernel.  When the segments
+// are about as many as the units (at least three quarters of them, at most
+// all) and none holds more than twice the mean chunks, unit w takes one
+// segment whole: no partials are written and the merge has nothing to do.
+// The balanced split would cut nearly every segment in two there, and the
+// partial writes and their merge cost more than the longest segment's
+// excess over the mean.  The longest segments go to the lowest unit
+// numbers, which the dispatcher starts first (later workgroups of a compute
+// unit start and step later).  Every unit takes the same decision from the
+// same lengths.  Needs at most 128 sequences (their lengths sit in the
+// lanes of c0 and c1) and one column block per (sequence, kv head); unit w
+// takes kv head w % Hkv of the sequence ranked w / Hkv.  Returns false for
+// the balanced split; otherwise pc is unit w's piece (no chunks for w >= the
+// segments), its segment's record written.
+__device__ bool whole_segment_piece(const StreamParams& p, int lane, bool leader, int w, int W, const SeqLens& c0,
+                                    const SeqLens& c1, PieceDesc& pc) {
+  if (!p.whole_ok || p.num_seqs > 128 || p.col_blocks != 1) return false;
+  const int S = p.num_seqs * p.num_kv_heads;
+  if (S > W || 4 * S < 3 * W) return false;
+  const int n0 = seg_chunks(c0.L, c0.Q, p.group, p.cols_per_block, 0);
+  const int n1 = seg_chunks(c1.L, c1.Q, p.group, p.cols_per_block, 0);
+  int mx = max(n0, n1);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  const int64_t sum = wave_sum64((int64_t)n0 + n1);
+  if ((int64_t)mx * p.num_seqs > 2 * sum) return false;
+  pc.c_end = 0;
+  if (w >= S) return true;
+  // rank of each lane's two sequences (lane and 64 + lane) by chunks,
+  // longest first, ties by sequence index
+  int rk0 = 0, rk1 = 0;
+  for (int j = 0; j < 64; ++j) {
+    const int a0 = __builtin_amdgcn_readlane(n0, j);
+    const int a1 = __builtin_amdgcn_readlane(n1, j);
+    rk0 += (a0 > n0 || (a0 == n0 && j < lane)) ? 1 : 0;
+    rk0 += (a1 > n0) ? 1 : 0;
+    rk1 += (a0 >= n1) ? 1 : 0;
+    rk1 += (a1 > n1 || (a1 == n1 && j < lane)) ? 1 : 0;
+  }
+  const int r = w / p.num_kv_heads;
+  const uint64_t hit0 = __builtin_amdgcn_ballot_w64(rk0 == r && lane < p.num_seqs);
+  const uint64_t hit1 = __builtin_amdgcn_ballot_w64(rk1 == r && 64 + lane < p.num_seqs);
+  const bool in0 = hit0 != 0;
+  const int src = in0 ? __builtin_ctzll(hit0) : __builtin_ctzll(hit1);
+  // the sequence's first query row: new tokens of the sequences before it
+  const int q0 = (int)wave_incl_scan64(c0.Q, lane);
+  const int q1 = (int)wave_incl_scan64(c1.Q, lane);
+  pc.b = (in0 ? 0 : 64) + src;
+  pc.h = w - r * p.num_kv_heads;
+  pc.cb = 0;
+  pc.L = in0 ? __shfl(c0.L, src) : __shfl(c1.L, src);
+  pc.Q = in0 ? __shfl(c0.Q, src) : __shfl(c1.Q, src);
+  pc.row0 = (in0 ? __shfl(q0, src) : __shfl(q0, 63) + __shfl(q1, src)) - pc.Q;
+  pc.c_begin = 0;
+  pc.c_end = in0 ? __shfl(n0, src) : __shfl(n1, src);
+  pc.whole = true;
+  const int seg = pc.b * p.num_kv_heads + pc.h;
+  pc.slot = seg + w;
+  pc.b = __builtin_amdgcn_readfirstlane(pc.b);
+  pc.L = __builtin_amdgcn_readfirstlane(pc.L);
+  pc.Q = __builtin_amdgcn_readfirstlane(pc.Q);
+  pc.row0 = __builtin_amdgcn_readfirstlane(pc.row0);
+  pc.c_end = __builtin_amdgcn_readfirstlane(pc.c_end);
+  pc.slot = __builtin_amdgcn_readfirstlane(pc.slot);
+  if (leader) p.seg_merge[seg] = make_int2(pc.slot, 1);
+  return true;
+}
+
 // ---- attention kernels -------------------------------------------------------
 // NCT = 0 is the packed decode layout (at most 4 query columns; each wave is
 // a unit) with PR groups in flight per wave, NCT = 1 one 16-column tile whose
@@ -1721,6 +1789,13 @@ __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void at
   const int64_t T = total_chunks(p, lane, c0, c1);
   const int W = work_units(p, T);
   if (w >= W) return;
+  PieceDesc whole;
+  if (whole_segment_piece(p, lane, leader, w, W, c0, c1, whole)) {
+    // its own inlined copy of the piece, specialised for a whole segment
+    if (whole.c_end > 0)
+      run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KF, TileCfg<NW, NT>::PP>(p, whole, lane, wave);
+    return;
+  }
   walk_pieces(p, lane, leader, w, W, T, c0, c1, [&](const PieceDesc& pc) {
     run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KF, TileCfg<NW, NT>::PP>(p, pc, lane, wave);
   });

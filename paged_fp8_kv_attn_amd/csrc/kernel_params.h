@@ -41,6 +41,7 @@ struct StreamParams {
   int32_t unit_min_chunks;     // units in use: total chunks / this, within [1, max_units]
   int32_t max_units;           // units sharing the chunks at most (waves or workgroups)
   int32_t start_cost;          // chunks a segment's start counts for in the balanced split
+  int32_t whole_ok;            // the tile kernel may give each unit one segment whole
   int64_t v_scale_offset;      // P * Hkv: start of the V scales in kv_scales
   float qk_scale_log2;         // sm_scale * log2(e)
 };

@@ -36,6 +36,30 @@ def plan_for(w, **over) -> Plan:
     return Plan(**kw)
 
 
+def whole_schedule_workload(B, lo, hi, *, seed, kv_format="e4m3", q_dtype="bf16", out_dtype="bf16"):
+    """MTP-verification-shaped batch (5 new tokens, 40 query heads on 8 kv
+    heads, head_dim 128) with B contexts drawn uniformly from [lo, hi]."""
+    from synth import custom_workload
+    ctx = np.random.default_rng(seed).integers(lo, hi + 1, size=B).tolist()
+    return custom_workload([5] * B, ctx, num_q_heads=40, num_kv_heads=8, head_dim=128, seed=seed,
+                           q_dtype=q_dtype, out_dtype=out_dtype, kv_format=kv_format, name=f"whole_s{seed}")
+
+
+def takes_whole_schedule(w, info) -> bool:
+    """Whether the shared-KV tile kernel gives each unit one segment whole on
+    workload w (one column block, 5 new tokens per sequence), restated from
+    the kernel's rule so that a change of the rule shows in the tests: at
+    most 128 sequences; units W = min(the plan's units, T / 16), T counting
+    each segment's chunks plus 3 for its start; 3 W <= 4 S <= 4 W for S
+    segments; the longest at most twice the mean."""
+    n = [-(-int(L) // 32) for L in w.ctx_lens]
+    S = len(n) * w.num_kv_heads
+    T = sum(w.num_kv_heads * (x + 3) for x in n)
+    W = min(info["work_units"], T // 16)
+    return bool(info["shared_kv"] and info["col_blocks"] == 1 and len(n) <= 128 and 3 * W <= 4 * S <= 4 * W
+                and max(n) * len(n) <= 2 * sum(n))
+
+
 def device_inputs(w, dev="cuda"):
     return dict(
         q=w.q.to(dev).contiguous(),

@@ -14,7 +14,8 @@ import oracle
 import oracle.attention as oracle_attention
 import paged_fp8_kv_attn_amd as pa
 from synth import custom_workload, make_workload
-from tests.gpu_helpers import check_contract, device_inputs, log, plan_for, run_gpu
+from tests.gpu_helpers import (check_contract, device_inputs, log, plan_for, run_gpu, takes_whole_schedule,
+                                whole_schedule_workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -160,3 +161,13 @@ def test_int4_garbage_does_not_leak():
             w.v_pages[last, :, s // 4, :, :, (s % 4) // 2] = (sub & keep) | noise
     got = run_gpu(w, plan=plan_for(w, kv_format="int4"))
     assert np.array_equal(got, ref)
+
+
+def test_int4_whole_segment_schedule():
+    # every unit takes one (sequence, kv head) segment whole
+    w = whole_schedule_workload(128, 300, 600, seed=960, kv_format="int4")
+    plan = plan_for(w, kv_format="int4")
+    info = plan.info()
+    plan.close()
+    assert takes_whole_schedule(w, info), info
+    _parity(w)

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 from synth import custom_workload, make_workload
-from tests.gpu_helpers import check_contract, log, plan_for, run_gpu
+from tests.gpu_helpers import (check_contract, log, plan_for, run_gpu, takes_whole_schedule,
+                                whole_schedule_workload)
 
 import oracle
 
@@ -81,4 +82,14 @@ def test_int8_edges(idx):
 def test_int8_forced_partitions():
     w = custom_workload([1, 1, 1], [1000, 37, 2048], num_q_heads=8, num_kv_heads=2, head_dim=128, seed=410,
                         num_kv_splits=7, kv_format="int8", name="int8_splits7")
+    _parity(w)
+
+
+def test_int8_whole_segment_schedule():
+    # every unit takes one (sequence, kv head) segment whole
+    w = whole_schedule_workload(128, 300, 600, seed=950, kv_format="int8")
+    plan = plan_for(w, kv_format="int8")
+    info = plan.info()
+    plan.close()
+    assert takes_whole_schedule(w, info), info
     _parity(w)

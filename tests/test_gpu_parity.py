@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from synth import custom_workload, make_workload
-from tests.gpu_helpers import check_contract, log, plan_for, record, run_gpu, run_oracle
+from tests.gpu_helpers import (check_contract, log, plan_for, record, run_gpu, run_oracle, takes_whole_schedule,
+                                whole_schedule_workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -122,6 +123,30 @@ def test_many_sequences(idx):
     w = custom_workload([ql] * B, ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, seed=700 + idx,
                         num_kv_splits=splits, name=f"many{idx}")
     assert w.num_seqs > 128
+    _parity(w)
+
+
+# Shapes on which the shared-KV tile kernel gives every unit one segment
+# whole (about as many (sequence, kv head) segments as units, none longer
+# than twice the mean): the two-wave tile on 25-column blocks, 4 resident
+# workgroups per compute unit.
+WHOLE = [
+    # (B, ctx range, q dtype, out dtype); 5 new tokens, 40 query heads / 8 kv heads
+    (128, (300, 600), "bf16", "bf16"),
+    (128, (500, 500), "bf16", "bf16"),   # equal lengths: ranked by sequence index
+    (128, (300, 600), "f32", "f32"),
+    (100, (300, 600), "bf16", "bf16"),   # 800 segments: some units idle
+]
+
+
+@pytest.mark.parametrize("idx", range(len(WHOLE)))
+def test_whole_segment_schedule(idx):
+    B, (lo, hi), qd, od = WHOLE[idx]
+    w = whole_schedule_workload(B, lo, hi, seed=900 + idx, q_dtype=qd, out_dtype=od)
+    plan = plan_for(w)
+    info = plan.info()
+    plan.close()
+    assert takes_whole_schedule(w, info), info
     _parity(w)
 
 

@@ -104,3 +104,91 @@ def test_empty_start_piece_is_possible_and_covered():
             found = True
             _check(real, 64, 1, 1)
     assert found
+
+
+# ---- whole-segment schedule of the shared-KV tile kernel --------------------
+# When the segments (one column block each) are at least 3/4 of the units W
+# and at most W, and the longest holds at most twice the mean chunks, unit w
+# takes kv head w % H of the sequence ranked w // H (most chunks first, ties
+# by index) whole.  The kernel ranks the sequences two per lane: lane i holds
+# sequences i and 64 + i and counts, over j < 64, the sequences that sort
+# before each of its own.
+
+def _kernel_ranks(n):
+    n = list(n) + [0] * (128 - len(n))
+    rk = [0] * 128
+    for lane in range(64):
+        n0, n1 = n[lane], n[64 + lane]
+        r0 = r1 = 0
+        for j in range(64):
+            a0, a1 = n[j], n[64 + j]
+            r0 += (a0 > n0 or (a0 == n0 and j < lane)) + (a1 > n0)
+            r1 += (a0 >= n1) + (a1 > n1 or (a1 == n1 and j < lane))
+        rk[lane], rk[64 + lane] = r0, r1
+    return rk
+
+
+def _whole_decision(n, H, W):
+    S = len(n) * H
+    if len(n) > 128 or S > W or 4 * S < 3 * W:
+        return False
+    return max(n) * len(n) <= 2 * sum(n)
+
+
+def _whole_units(n, H, W):
+    """The piece of each unit as the kernel builds it: (sequence, kv head,
+    first chunk, end chunk), or None for units past the segments."""
+    B = len(n)
+    rk = _kernel_ranks(n)[:B]
+    out = []
+    for w in range(W):
+        if w >= B * H:
+            out.append(None)
+            continue
+        r, h = divmod(w, H)
+        b = rk.index(r)
+        out.append((b, h, 0, n[b]))
+    return out
+
+
+def test_kernel_ranks_are_the_stable_descending_order():
+    rng = random.Random(11)
+    for _ in range(300):
+        B = rng.randint(1, 128)
+        n = [rng.choice([rng.randint(0, 3), rng.randint(1, 40), 7]) for _ in range(B)]
+        rk = _kernel_ranks(n)[:B]
+        order = sorted(range(B), key=lambda i: (-n[i], i))
+        assert [rk[i] for i in order] == list(range(B))
+
+
+def test_whole_segment_units_cover_each_segment_once():
+    rng = random.Random(200)
+    seen = 0
+    for _ in range(300):
+        H = rng.choice([1, 2, 8])
+        B = rng.randint(1, 128)
+        W = rng.choice([B * H, B * H + rng.randint(0, B * H // 3), 1024])
+        lo_n = rng.randint(1, 20)
+        n = [rng.choice([0, rng.randint(lo_n, 2 * lo_n)]) if rng.random() < 0.05 else rng.randint(lo_n, 2 * lo_n)
+             for _ in range(B)]
+        if not _whole_decision(n, H, W):
+            continue
+        seen += 1
+        units = _whole_units(n, H, W)
+        got = sorted(u for u in units if u is not None and u[3] > u[2])
+        assert got == [(b, h, 0, n[b]) for b in range(B) for h in range(H) if n[b] > 0]
+        # longest first: unit numbers rise as the segments shorten
+        lens = [u[3] for u in units if u is not None]
+        assert lens == sorted(lens, reverse=True)
+    assert seen > 50
+
+
+def test_whole_decision_on_the_named_shapes():
+    rng = random.Random(5)
+    # MTP verification: 128 sequences x 8 kv heads, 5 new tokens, 128-1152 keys
+    n = [(rng.randint(128, 1152) + 31) // 32 for _ in range(128)]
+    assert _whole_decision(n, 8, 1024)
+    # one long sequence among short ones stays with the balanced split
+    assert not _whole_decision([4] * 127 + [400], 8, 1024)
+    # fewer segments than three quarters of the units (MQA decode, 64 x 1)
+    assert not _whole_decision([100] * 64, 1, 512)
