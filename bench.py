@@ -476,6 +476,143 @@ class HipGraph:
             self._graph = self._c.c_void_p()
 
 
+def timeline_stats(a: np.ndarray, info: dict) -> dict:
+    """Summary of one forward's timeline rows (int64 [rows][TIMELINE_WORDS],
+    attn_plan_set_timeline): the unit of the schedule is a wave of the packed
+    decode or a workgroup otherwise (its wave 0 stands for it); times in us
+    from the first wave's start."""
+    words = a.shape[1]
+    u = a.view(np.uint64)
+    typ = (u & np.uint64(15)).astype(np.int64)
+    tim = (u >> np.uint64(4)).astype(np.int64)
+    per_us = info["wallclock_khz"] / 1e3
+    wpg = info["waves_per_group"]
+    packed = info["packed"] > 0
+    ran = typ[:, 0] == 1
+    t0 = tim[ran, 0].min()
+    us = lambda x: (x - t0) / per_us  # noqa: E731
+    units = []
+    for r in np.nonzero(ran)[0]:
+        if not packed and r % wpg:
+            continue
+        ev = [(int(typ[r, i]), us(tim[r, i])) for i in range(words - 1) if typ[r, i] != 0]
+        steps = [t for k, t in ev if k == 4]
+        pieces, cur = [], None
+        for k, t in ev:
+            if k == 3:
+                cur = {"start": t, "steps": []}
+            elif k == 4 and cur is not None:
+                cur["steps"].append(t)
+            elif k == 5 and cur is not None:
+                cur["end"] = t
+                pieces.append(cur)
+                cur = None
+        gaps = [b - a_ for p_ in pieces for a_, b in zip(p_["steps"], p_["steps"][1:])]
+        restarts = [nx["steps"][0] - pv["end"] for pv, nx in zip(pieces, pieces[1:]) if nx["steps"]]
+        units.append({"slot": (r // wpg) // max(1, info["compute_units"]), "first": steps[0] if steps else np.nan,
+                      "end": us(tim[r, -1]) if typ[r, -1] == 7 else np.nan, "steps": len(steps),
+                      "pieces": len(pieces), "gap": float(np.median(gaps)) if gaps else np.nan,
+                      "restarts": restarts, "full": len(ev) >= words - 1})
+    busy = [x for x in units if x["steps"] > 0]
+    f = np.array([x["first"] for x in busy])
+    e = np.array([x["end"] for x in busy])
+    g = np.array([x["gap"] for x in busy if np.isfinite(x["gap"])])
+    rs = np.array([t for x in busy for t in x["restarts"]])
+    pct = lambda v, q: float(np.percentile(v, q)) if len(v) else None  # noqa: E731
+
+    def corr(key):
+        v = np.array([x[key] for x in busy], dtype=float)
+        return float(np.corrcoef(v, e)[0, 1]) if len(v) > 2 and np.std(v) > 0 and np.std(e) > 0 else None
+
+    slots = sorted({x["slot"] for x in busy})
+    return {
+        "units": len(units), "units_with_chunks": len(busy),
+        "rows_full": int(sum(x["full"] for x in units)),
+        "span_us": float(np.nanmax([x["end"] for x in units])),
+        "first_step_us": {"p10": pct(f, 10), "median": pct(f, 50), "p90": pct(f, 90)},
+        "step_interval_us": {"p10": pct(g, 10), "median": pct(g, 50), "p90": pct(g, 90)},
+        "end_us": {"min": pct(e, 0), "median": pct(e, 50), "max": pct(e, 100)},
+        "restart_us": {"count": int(len(rs)), "median": pct(rs, 50)},
+        "end_corr": {"dispatch_slot": corr("slot"), "first_step": corr("first"), "pieces": corr("pieces"),
+                     "steps": corr("steps"), "step_interval": corr("gap")},
+        "by_slot": {str(sl): {"units": int(sum(x["slot"] == sl for x in busy)),
+                              "first_step_median_us": pct([x["first"] for x in busy if x["slot"] == sl], 50),
+                              "end_median_us": pct([x["end"] for x in busy if x["slot"] == sl], 50)}
+                    for sl in slots},
+    }
+
+
+def record_timelines(pt, graph, stream, graph_ms: float, args, n: int = 3) -> dict:
+    """Three more forwards of part `pt`, each with the timeline hook on and
+    queued behind replays of the timed steps (so the GPU is in the timed
+    state when it starts); returns their summaries and the per-key medians,
+    and writes the text summary to args.timeline_summary."""
+    import torch
+    from paged_fp8_kv_attn_amd import TIMELINE_WORDS
+
+    info = pt.plan.info()
+    rows = torch.zeros(info["grid_size"] * info["waves_per_group"] * TIMELINE_WORDS, dtype=torch.int64,
+                       device=pt.q.device)
+    runs = []
+    for i in range(n):
+        rows.zero_()
+        torch.cuda.synchronize()
+        if graph is not None:
+            for _ in range(max(1, math.ceil(2.0 / max(graph_ms, 1e-6)))):
+                graph.launch(stream)
+        pt.plan.set_timeline(rows)
+        pt.forward(i + 1, stream)
+        pt.plan.set_timeline(None)
+        torch.cuda.synchronize()
+        runs.append(timeline_stats(rows.view(-1, TIMELINE_WORDS).cpu().numpy(), info))
+
+    def med(path):
+        vals = []
+        for r in runs:
+            v = r
+            for k in path:
+                v = v.get(k) if isinstance(v, dict) else None
+            if v is not None:
+                vals.append(v)
+        return float(np.median(vals)) if vals else None
+
+    keys = [("span_us",), ("first_step_us", "p10"), ("first_step_us", "median"), ("first_step_us", "p90"),
+            ("step_interval_us", "p10"), ("step_interval_us", "median"), ("step_interval_us", "p90"),
+            ("end_us", "min"), ("end_us", "median"), ("end_us", "max"), ("restart_us", "median"),
+            ("end_corr", "dispatch_slot"), ("end_corr", "first_step"), ("end_corr", "pieces"),
+            ("end_corr", "steps"), ("end_corr", "step_interval")]
+    medians = {".".join(k): med(k) for k in keys}
+    kern = attention_kernel_name(info)
+    xf = f" --kv-format {args.kv_format}" if args.kv_format != "e4m3" else ""
+    lines = [f"# Per-wave timeline of {kern}, workload {args.workload} (MI355X, gfx950), recorded by the kernels "
+             f"through attn_plan_set_timeline",
+             f"# command: python bench.py --workload {args.workload}{xf} --steps {args.steps} --warmup {args.warmup} "
+             f"--reps {args.reps} --no-cpu-baseline --timeline-summary <this file>",
+             f"# kernel_source_sha256_16: {source_hash(KERNEL_SOURCE)}",
+             f"# counter: s_memrealtime at {info['wallclock_khz']} kHz; {n} forwards, each queued behind replays "
+             f"of the timed steps; times in us from the kernel's first wave start; a unit is a wave (packed "
+             f"decode) or a workgroup (its wave 0); dispatch slot = workgroup // compute units; first step = the "
+             f"unit's first chunk step; step interval = median gap between consecutive chunk steps of a piece; "
+             f"restart = from a piece's end to the next piece's first step; end_corr = correlation of the "
+             f"units' end times with each quantity; the recording runs copies of the kernels with the "
+             f"recording compiled in, whose per-event stores make them a few percent slower than the "
+             f"kernels forwards otherwise run",
+             f"plan: grid {info['grid_size']} waves_per_group {info['waves_per_group']} packed {info['packed']} "
+             f"shared_kv {info['shared_kv']} units {runs[0]['units']} with chunks {runs[0]['units_with_chunks']} "
+             f"rows full {runs[0]['rows_full']}"]
+    for k, v in medians.items():
+        lines.append(f"median_{k}: {v:.3f}" if v is not None else f"median_{k}: none")
+    for sl, d in runs[0]["by_slot"].items():
+        fs = d["first_step_median_us"]
+        en = d["end_median_us"]
+        lines.append(f"forward0_slot{sl}: units {d['units']} first_step_median_us "
+                     f"{fs:.2f} end_median_us {en:.2f}" if fs is not None and en is not None
+                     else f"forward0_slot{sl}: units {d['units']}")
+    with open(args.timeline_summary, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return {"medians": medians, "forwards": runs}
+
+
 def cpu_baseline(w, counts, budget_s: float) -> dict:
     """Time the oracle (as it stands) on the host over whole passes of the
     workload's sequences until about budget_s seconds have been spent."""
@@ -552,6 +689,9 @@ def main():
                     help="KV format of the attention workloads (INT8: two's-complement bytes times the page "
                          "scale; INT4: two 4-bit codes per byte, attention workloads of head_dim 128 only)")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--timeline-summary", default=None,
+                    help="attention workloads: record per-wave timelines of three more forwards "
+                         "(attn_plan_set_timeline) and write their summary here")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -789,6 +929,10 @@ def main():
         for e in starts + stops + (me[0] + me[1] if me is not None else []):
             hipt.destroy_event(e)
 
+    timeline = None
+    if args.timeline_summary and all(isinstance(pt, Part) for pt in parts):
+        timeline = record_timelines(parts[0], graph, stream, ms * args.steps, args)
+
     def roofline(pt, traffic):
         c = pt.counts
         k_gbs = c["bytes"] / (pt.attn_ms * 1e-3) / 1e9
@@ -880,6 +1024,8 @@ def main():
         res["cpu_baseline"] = cpu_baseline(dom.w, dom.counts, args.cpu_seconds)
         if len(parts) > 1:
             res["cpu_baseline"]["sample"] += f" (workload part {dom.w.name})"
+    if timeline is not None:
+        res["timeline"] = timeline
     line = json.dumps(res)
     print(line, flush=True)
     if args.json_out:

@@ -160,6 +160,7 @@ typedef struct {
   int32_t resident_groups_per_cu; /* attention workgroups one compute unit holds at once */
   int32_t compute_units;          /* of the plan's device */
   size_t workspace_bytes;         /* device bytes owned by the plan */
+  int32_t wallclock_khz;          /* rate of the counter attn_plan_set_timeline records */
 } attn_plan_info_t;
 
 /* Validate desc, choose tiles/splits, allocate the workspace once with
@@ -201,6 +202,26 @@ attn_status_t attn_plan_set_kernel_events(attn_plan_t plan, hipEvent_t attention
  * A forward that launches no merge records both events at the same point of
  * the stream (zero duration). */
 attn_status_t attn_plan_set_merge_events(attn_plan_t plan, hipEvent_t merge_start, hipEvent_t merge_stop);
+
+/* Measurement hook.  With `rows` non-null, every later forward on this plan
+ * has each wave of its attention kernel record a timeline in its own row of
+ * ATTN_TIMELINE_WORDS uint64 words of `rows` (device memory, 8-byte
+ * aligned): row = workgroup * waves_per_group + wave, num_rows at least
+ * grid_size * waves_per_group (attn_plan_get_info), else
+ * ATTN_ERR_INVALID_ARGUMENT.  Word i < ATTN_TIMELINE_WORDS - 1 is the i-th
+ * event, (t << 4) | type, t the GPU's constant-rate real-time counter
+ * (wallclock_khz ticks per millisecond): type 1 the wave's start, 2 its
+ * chunk range known, then per piece of a segment 3 its start, 4 each chunk
+ * step (each group of chunks in the packed decode), 5 its end; events past
+ * the row's first ATTN_TIMELINE_WORDS - 1 words are dropped.  The last word
+ * is (t << 4) | 7 at the wave's end.  Words nothing writes keep their
+ * contents: zero the rows before the forward.  Null turns it off.  The
+ * forwards then run copies of the attention kernels built with the
+ * recording (the others contain none of it), for E4M3 KV with bf16 q and
+ * out only: other plans get ATTN_ERR_UNSUPPORTED.  The buffer stays owned
+ * by the caller and must outlive its use. */
+#define ATTN_TIMELINE_WORDS 64
+attn_status_t attn_plan_set_timeline(attn_plan_t plan, uint64_t* rows, size_t num_rows);
 
 /* ---- allocation-free forward ----
  * For callers that cannot allocate device memory: code under HIP graph

@@ -6,6 +6,7 @@ There is no CPU fallback: without the built library every call raises.
 """
 
 from ._binding import (  # noqa: F401
+    TIMELINE_WORDS,
     AttnError,
     Plan,
     PlanInfo,

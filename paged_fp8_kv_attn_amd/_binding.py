@@ -13,6 +13,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpagedattn.so"
+TIMELINE_WORDS = 64  # words per wave in a timeline row (ATTN_TIMELINE_WORDS)
 
 ATTN_DTYPE_F32 = 0
 ATTN_DTYPE_BF16 = 1
@@ -26,6 +27,7 @@ _FUNCTIONS = [
     "attn_plan_get_info",
     "attn_plan_set_kernel_events",
     "attn_plan_set_merge_events",
+    "attn_plan_set_timeline",
     "attn_status_string",
     "attn_last_hip_error",
     "attn_debug_gather",
@@ -87,6 +89,7 @@ class PlanInfo(ctypes.Structure):
         ("resident_groups_per_cu", ctypes.c_int32),
         ("compute_units", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
+        ("wallclock_khz", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -122,6 +125,8 @@ def load_library():
     lib.attn_plan_set_kernel_events.restype = i32
     lib.attn_plan_set_merge_events.argtypes = [vp, vp, vp]
     lib.attn_plan_set_merge_events.restype = i32
+    lib.attn_plan_set_timeline.argtypes = [vp, vp, ctypes.c_size_t]
+    lib.attn_plan_set_timeline.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -350,6 +355,22 @@ class Plan:
         forward (a forward without a merge records both at one point)."""
         _check(load_library().attn_plan_set_merge_events(self._h, _event(start), _event(stop)),
                "attn_plan_set_merge_events")
+
+    def set_timeline(self, rows=None):
+        """Have every later forward record its attention kernel's per-wave
+        timeline into `rows`, an int64 tensor on the plan's device with at
+        least grid_size * waves_per_group rows of TIMELINE_WORDS words
+        (zeroed by the caller before each forward); None stops recording."""
+        if rows is None:
+            _check(load_library().attn_plan_set_timeline(self._h, None, 0), "attn_plan_set_timeline")
+            self._timeline = None
+            return
+        inf = self.info()
+        need = inf["grid_size"] * inf["waves_per_group"]
+        _want(rows, "timeline rows", self.device, (torch.int64,), min_numel=need * TIMELINE_WORDS)
+        _check(load_library().attn_plan_set_timeline(self._h, _ptr(rows), rows.numel() // TIMELINE_WORDS),
+               "attn_plan_set_timeline")
+        self._timeline = rows  # kept alive while the library holds its address
 
     def forward(self, q, k_pages, v_pages, kv_scales, block_table, ctx_lens, q_lens, out, stream=None):
         check_forward_tensors(self.desc, self.device, q, k_pages, v_pages, kv_scales, block_table, ctx_lens,

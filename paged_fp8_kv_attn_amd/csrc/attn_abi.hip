@@ -34,6 +34,8 @@ struct attn_plan_s {
   int unit_min_chunks;  // chunks per unit at least (within [1, max_units] units)
   int start_cost;       // chunks a segment's start counts for in the balanced split
   bool whole_ok;        // the tile kernel may give each unit one segment whole
+  uint64_t* timeline;   // null, or the caller's timeline rows
+  int wallclock_khz;    // rate of the timeline's counter
   int occupancy;     // resident attention workgroups per compute unit
   int num_cus;
   float sm_scale;
@@ -232,6 +234,10 @@ attn_status_t choose_plan(const attn_plan_desc_t& d, int device, attn_plan_s* p)
   // 48.6-49.0 us; the merge finds nothing to do).  Not with a forced split
   // count.
   p->whole_ok = d.num_kv_splits == 0 && v.tile_waves > 0;
+  p->timeline = nullptr;
+  p->wallclock_khz = 0;
+  if (hipDeviceGetAttribute(&p->wallclock_khz, hipDeviceAttributeWallClockRate, device) != hipSuccess)
+    p->wallclock_khz = 0;
   p->grid = static_cast<int>(ceil_div(units * unit_waves, wpg));
   // merge: one workgroup per segment (and slice of its columns); segments
   // with many pieces on average get fewer columns per workgroup
@@ -305,6 +311,7 @@ attn_status_t enqueue_forward(const attn_plan_s* plan, const void* q, const uint
   sp.max_units = plan->max_units;
   sp.start_cost = plan->start_cost;
   sp.whole_ok = plan->whole_ok ? 1 : 0;
+  sp.timeline = reinterpret_cast<unsigned long long*>(plan->timeline);
   sp.seq_row0 = plan->seq_row0;
   sp.seg_merge = plan->seg_merge;
   sp.v_scale_offset = static_cast<int64_t>(d.num_pages) * d.num_kv_heads;
@@ -420,6 +427,20 @@ attn_status_t attn_plan_get_info(attn_plan_t plan, attn_plan_info_t* info) {
   info->resident_groups_per_cu = plan->occupancy;
   info->compute_units = plan->num_cus;
   info->workspace_bytes = plan->workspace_bytes;
+  info->wallclock_khz = plan->wallclock_khz;
+  return ATTN_OK;
+}
+
+static_assert(pa::kTimelineSlots == ATTN_TIMELINE_WORDS, "timeline row length");
+
+attn_status_t attn_plan_set_timeline(attn_plan_t plan, uint64_t* rows, size_t num_rows) {
+  if (!plan) return ATTN_ERR_INVALID_ARGUMENT;
+  if (rows) {
+    if (!pa::timeline_supported(plan->variant)) return ATTN_ERR_UNSUPPORTED;
+    const size_t need = static_cast<size_t>(plan->grid) * pa::waves_per_group(plan->variant);
+    if (num_rows < need || !aligned(rows, 8)) return ATTN_ERR_INVALID_ARGUMENT;
+  }
+  plan->timeline = rows;
   return ATTN_OK;
 }
 

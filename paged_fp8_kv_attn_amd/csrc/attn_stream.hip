@@ -264,14 +264,15 @@ struct SeqStart {
 
 // Total chunks over all sequences (wave-uniform); `c0` and `c1` hold
 // sequences 0 .. 63 and 64 .. 127 (loaded together at the kernel's start).
-__device__ int64_t total_chunks(const StreamParams& p, int lane, const SeqLens& c0, const SeqLens& c1) {
+__device__ __forceinline__ int64_t total_chunks(const StreamParams& p, int lane, const SeqLens& c0, const SeqLens& c1) {
   int64_t total = wave_sum64(c0.nb) + wave_sum64(c1.nb);
   for (int base = 128; base < p.num_seqs; base += 64) total += wave_sum64(load_seq(p, base + lane).nb);
   return total;
 }
 
 // The sequence whose chunks contain global chunk `pos` (< total).
-__device__ SeqStart locate_seq(const StreamParams& p, int64_t pos, int lane, const SeqLens& c0, const SeqLens& c1) {
+__device__ __forceinline__ SeqStart locate_seq(const StreamParams& p, int64_t pos, int lane, const SeqLens& c0,
+                                                const SeqLens& c1) {
   int64_t carry = 0;
   int rows = 0;
   for (int base = 0; base < p.num_seqs; base += 64) {
@@ -299,7 +300,7 @@ __device__ SeqStart locate_seq(const StreamParams& p, int64_t pos, int lane, con
 
 // Workgroup 0 records the first query row of every sequence for the merge
 // kernel, which runs after this kernel on the same stream.
-__device__ void write_seq_meta(const StreamParams& p, int lane) {
+__device__ __forceinline__ void write_seq_meta(const StreamParams& p, int lane) {
   int rows = 0;
   for (int base = 0; base < p.num_seqs; base += 64) {
     const int b = base + lane;
@@ -387,8 +388,49 @@ struct PieceDesc {
   int slot;            // partial slot when not whole
 };
 
-template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int NBUF, int KF>
-__device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc& pc, int lane, int wave) {
+// Measurement: the kernels instantiated with ON record, for every wave, events
+// in its own row of kTimelineSlots words of p.timeline (row = workgroup x
+// waves per workgroup + wave), each (s_memrealtime << 4) | type, in order:
+// kTlEntry, kTlScheduled (its unit's range known), then per piece
+// kTlPieceStart, kTlStep per chunk (per group of chunks in the packed
+// decode), kTlPieceEnd; the row's last word holds kTlWaveEnd.  Events past
+// the row's first kTimelineSlots - 1 words are dropped.  Lane 0 writes;
+// the count is the same in every lane.  The kernels without ON (the ones
+// forwards use unless a timeline is set) contain none of it: a run-time
+// check per chunk step measured 1-4% slower.
+enum : unsigned { kTlEntry = 1, kTlScheduled = 2, kTlPieceStart = 3, kTlStep = 4, kTlPieceEnd = 5, kTlWaveEnd = 7 };
+template <bool ON>
+struct Timeline {
+  unsigned long long* row;
+  int n;
+  __device__ __forceinline__ void rec(unsigned type, int lane) {
+    if constexpr (ON) {
+      if (n < kTimelineSlots - 1) {
+        const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+        if (lane == 0) row[n] = (t << 4) | type;
+        ++n;
+      }
+    }
+  }
+  __device__ __forceinline__ void end(int lane) {
+    if constexpr (ON) {
+      const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+      if (lane == 0) row[kTimelineSlots - 1] = (t << 4) | kTlWaveEnd;
+    }
+  }
+};
+
+template <bool ON>
+__device__ __forceinline__ Timeline<ON> timeline_for(const StreamParams& p, int wave) {
+  Timeline<ON> tl;
+  tl.row = ON ? p.timeline + ((size_t)blockIdx.x * (blockDim.x / 64) + wave) * kTimelineSlots : nullptr;
+  tl.n = 0;
+  return tl;
+}
+
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int NBUF, int KF, class TLT>
+__device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc& pc, int lane, int wave, TLT& tl) {
+  tl.rec(kTlPieceStart, lane);
   using GD = Geo<D>;
   using KL = KvLoads<D, KF>;
   constexpr int NW = kWavesPerGroup;
@@ -535,6 +577,7 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
 
   // compute chunk k from its ring slot
   auto step = [&](int k, int j) {
+    tl.rec(kTlStep, lane);
     const u32x4 (&kc)[2][KL::NK] = kbuf[j];
     const u32x4 (&vc)[2][KL::NV] = vbuf[j];
     const float (&skc)[2] = skb[j];
@@ -758,6 +801,7 @@ __device__ __forceinline__ void run_piece(const StreamParams& p, const PieceDesc
       }
     }
   }
+  tl.rec(kTlPieceEnd, lane);
 }
 
 // ---- packed decode piece: at most 4 query columns --------------------------
@@ -788,8 +832,9 @@ __device__ __forceinline__ float dpp_ror8(float x) {
   return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x128 /*row_ror:8*/, 0xf, 0xf, false));
 }
 
-template <int D, bool QF32, bool OUTF32, int NRING, int KF>
-__device__ __forceinline__ void run_piece_packed(const StreamParams& p, const PieceDesc& pc, int lane) {
+template <int D, bool QF32, bool OUTF32, int NRING, int KF, class TLT>
+__device__ __forceinline__ void run_piece_packed(const StreamParams& p, const PieceDesc& pc, int lane, TLT& tl) {
+  tl.rec(kTlPieceStart, lane);
   using GD = Geo<D>;
   using KL = KvLoads<D, KF>;
   constexpr int NP = QF32 ? 3 : 1;
@@ -921,6 +966,7 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
   };
 
   auto step = [&](int k, int j) {
+    tl.rec(kTlStep, lane);
     const u32x4 (&kc)[4][KL::NK] = kbuf[j];
     const u32x4 (&vc)[4][KL::NV] = vbuf[j];
     const float skl = skb[j];
@@ -1073,6 +1119,7 @@ __device__ __forceinline__ void run_piece_packed(const StreamParams& p, const Pi
       }
     }
   }
+  tl.rec(kTlPieceEnd, lane);
 }
 
 
@@ -1191,8 +1238,10 @@ __device__ __forceinline__ void load_q_operand(const StreamParams& p, size_t qof
   }
 }
 
-template <int D, int NW, int NT, bool QF32, bool OUTF32, int R, int KF, bool PP>
-__device__ __forceinline__ void run_piece_tile(const StreamParams& p, const PieceDesc& pc, int lane, int wave) {
+template <int D, int NW, int NT, bool QF32, bool OUTF32, int R, int KF, bool PP, class TLT>
+__device__ __forceinline__ void run_piece_tile(const StreamParams& p, const PieceDesc& pc, int lane, int wave,
+                                               TLT& tl) {
+  tl.rec(kTlPieceStart, lane);
   using GD = Geo<D>;
   using TG = TileGeo<D, NW, KF>;
   using KL = KvLoads<D, KF>;
@@ -1477,6 +1526,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
   if constexpr (!PP) {
     auto compute = [&](int k) {
       lds_barrier();
+      tl.rec(kTlStep, lane);
       f32x4 sacc[2][NT];
       bf16x8 pop_hi[NT], pop_lo[NT];
       qk(k, sacc);
@@ -1489,6 +1539,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
     bf16x8 pop_hi[NT], pop_lo[NT];
     auto compute = [&](int k) {
       lds_barrier();
+      tl.rec(kTlStep, lane);
       if (k > 0) pv(k - 1, pop_hi, pop_lo);
       f32x4 sacc[2][NT];
       qk(k, sacc);
@@ -1502,6 +1553,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
     ChunkMeta cm_prev;
     auto compute = [&](int k) {
       lds_barrier();
+      tl.rec(kTlStep, lane);
       if (k > 0) {
         bf16x8 pop_hi[NT], pop_lo[NT];
         softmax(k - 1, cm_prev, sacc, pop_hi, pop_lo);
@@ -1570,6 +1622,7 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
       }
     }
   }
+  tl.rec(kTlPieceEnd, lane);
 }
 
 }  // namespace
@@ -1671,8 +1724,8 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
 // takes kv head w % Hkv of the sequence ranked w / Hkv.  Returns false for
 // the balanced split; otherwise pc is unit w's piece (no chunks for w >= the
 // segments), its segment's record written.
-__device__ bool whole_segment_piece(const StreamParams& p, int lane, bool leader, int w, int W, const SeqLens& c0,
-                                    const SeqLens& c1, PieceDesc& pc) {
+__device__ __forceinline__ bool whole_segment_piece(const StreamParams& p, int lane, bool leader, int w, int W,
+                                                    const SeqLens& c0, const SeqLens& c1, PieceDesc& pc) {
   if (!p.whole_ok || p.num_seqs > 128 || p.col_blocks != 1) return false;
   const int S = p.num_seqs * p.num_kv_heads;
   if (S > W || 4 * S < 3 * W) return false;
@@ -1731,7 +1784,7 @@ __device__ bool whole_segment_piece(const StreamParams& p, int lane, bool leader
 // 4 waves take the chunks of a piece in turn (the workgroup is the unit).
 // Two waves per SIMD (256 registers each), one for the packed layout with
 // two groups in flight.
-template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int PR, int KF>
+template <int D, int NCT, bool DUPLO, bool QF32, bool OUTF32, int PR, int KF, bool TL = false>
 __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
                              (NCT == 0 ? (PR == 1 ? 2 : 1) : 2)) void attn_stream_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
@@ -1739,20 +1792,25 @@ __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
   const int w = (NCT == 0) ? (int)blockIdx.x * kPackedWaves + wave : (int)blockIdx.x;
   const bool leader = lane == 0 && (NCT == 0 || wave == 0);
 
+  Timeline<TL> tl = timeline_for<TL>(p, wave);
+  tl.rec(kTlEntry, lane);
   if (blockIdx.x == 0 && wave == 0) write_seq_meta(p, lane);
   const SeqLens c0 = load_seq(p, lane);
   const SeqLens c1 = load_seq(p, 64 + lane);
   const int64_t T = total_chunks(p, lane, c0, c1);
   const int W = work_units(p, T);
-  if (w >= W) return;
-  walk_pieces(p, lane, leader, w, W, T, c0, c1, [&](const PieceDesc& pc) {
-    if constexpr (NCT == 0) {
-      // at most 4 query columns: four pages per score tile
-      run_piece_packed<D, QF32, OUTF32, PR, KF>(p, pc, lane);
-    } else {
-      run_piece<D, NCT, DUPLO, QF32, OUTF32, 2, KF>(p, pc, lane, wave);
-    }
-  });
+  tl.rec(kTlScheduled, lane);
+  if (w < W) {
+    walk_pieces(p, lane, leader, w, W, T, c0, c1, [&](const PieceDesc& pc) {
+      if constexpr (NCT == 0) {
+        // at most 4 query columns: four pages per score tile
+        run_piece_packed<D, QF32, OUTF32, PR, KF>(p, pc, lane, tl);
+      } else {
+        run_piece<D, NCT, DUPLO, QF32, OUTF32, 2, KF>(p, pc, lane, wave, tl);
+      }
+    });
+  }
+  tl.end(lane);
 }
 
 // Wide column blocks: NW waves share each chunk through LDS, NT tiles each,
@@ -1776,29 +1834,38 @@ struct TileCfg {
   static constexpr bool PP = TILE_PINGPONG && NW == 8;
 };
 
-template <int D, int NW, int NT, bool QF32, bool OUTF32, int KF>
+template <int D, int NW, int NT, bool QF32, bool OUTF32, int KF, bool TL = false>
 __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void attn_tile_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int w = blockIdx.x;
   const bool leader = lane == 0 && wave == 0;
 
+  Timeline<TL> tl = timeline_for<TL>(p, wave);
+  tl.rec(kTlEntry, lane);
   if (w == 0 && wave == 0) write_seq_meta(p, lane);
   const SeqLens c0 = load_seq(p, lane);
   const SeqLens c1 = load_seq(p, 64 + lane);
   const int64_t T = total_chunks(p, lane, c0, c1);
   const int W = work_units(p, T);
-  if (w >= W) return;
-  PieceDesc whole;
-  if (whole_segment_piece(p, lane, leader, w, W, c0, c1, whole)) {
-    // its own inlined copy of the piece, specialised for a whole segment
-    if (whole.c_end > 0)
-      run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KF, TileCfg<NW, NT>::PP>(p, whole, lane, wave);
-    return;
+  if (w < W) {
+    PieceDesc whole;
+    if (whole_segment_piece(p, lane, leader, w, W, c0, c1, whole)) {
+      tl.rec(kTlScheduled, lane);
+      // its own inlined copy of the piece, specialised for a whole segment
+      if (whole.c_end > 0)
+        run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KF, TileCfg<NW, NT>::PP>(p, whole, lane, wave,
+                                                                                             tl);
+    } else {
+      tl.rec(kTlScheduled, lane);
+      walk_pieces(p, lane, leader, w, W, T, c0, c1, [&](const PieceDesc& pc) {
+        run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KF, TileCfg<NW, NT>::PP>(p, pc, lane, wave, tl);
+      });
+    }
+  } else {
+    tl.rec(kTlScheduled, lane);  // an empty range
   }
-  walk_pieces(p, lane, leader, w, W, T, c0, c1, [&](const PieceDesc& pc) {
-    run_piece_tile<D, NW, NT, QF32, OUTF32, TileCfg<NW, NT>::R, KF, TileCfg<NW, NT>::PP>(p, pc, lane, wave);
-  });
+  tl.end(lane);
 }
 
 // ---- log-sum-exp merge of the partials of one segment ---------------------
@@ -1921,8 +1988,14 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(StreamParams
 
 // ---- dispatch --------------------------------------------------------------
 
+// With tl, the kernels that record a timeline: built for E4M3 KV with bf16
+// Q and output only (nullptr otherwise).
 template <int D, int NCT, bool DUPLO, int PR = 1>
-static const void* kernel_d(const Variant& v) {
+static const void* kernel_d(const Variant& v, bool tl) {
+  if (tl) {
+    if (v.kv_format != kKvE4M3 || v.q_f32 || v.out_f32) return nullptr;
+    return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR, kKvE4M3, true>);
+  }
   // INT8 and INT4 KV: bf16 Q and output only (the plan rejects the rest)
   if (v.kv_format == kKvInt8)
     return reinterpret_cast<const void*>(&attn_stream_kernel<D, NCT, DUPLO, false, false, PR, kKvInt8>);
@@ -1939,7 +2012,11 @@ static const void* kernel_d(const Variant& v) {
 }
 
 template <int D, int NW, int NT>
-static const void* tile_d(const Variant& v) {
+static const void* tile_d(const Variant& v, bool tl) {
+  if (tl) {
+    if (v.kv_format != kKvE4M3 || v.q_f32 || v.out_f32) return nullptr;
+    return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, kKvE4M3, true>);
+  }
   if (v.kv_format == kKvInt8) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, kKvInt8>);
   if (v.kv_format == kKvInt4) {
     if constexpr (D == 128) return reinterpret_cast<const void*>(&attn_tile_kernel<D, NW, NT, false, false, kKvInt4>);
@@ -1952,21 +2029,21 @@ static const void* tile_d(const Variant& v) {
 }
 
 template <int D>
-static const void* kernel_tiles(const Variant& v) {
-  if (v.packed) return v.packed_ring == 2 ? kernel_d<D, 0, false, 2>(v) : kernel_d<D, 0, false, 1>(v);
-  if (v.tile_waves == 2 && v.col_tiles == 1) return tile_d<D, 2, 1>(v);
-  if (v.tile_waves == 4 && v.col_tiles == 1) return tile_d<D, 4, 1>(v);
-  if (v.tile_waves == 4 && v.col_tiles == 2) return tile_d<D, 4, 2>(v);
+static const void* kernel_tiles(const Variant& v, bool tl) {
+  if (v.packed) return v.packed_ring == 2 ? kernel_d<D, 0, false, 2>(v, tl) : kernel_d<D, 0, false, 1>(v, tl);
+  if (v.tile_waves == 2 && v.col_tiles == 1) return tile_d<D, 2, 1>(v, tl);
+  if (v.tile_waves == 4 && v.col_tiles == 1) return tile_d<D, 4, 1>(v, tl);
+  if (v.tile_waves == 4 && v.col_tiles == 2) return tile_d<D, 4, 2>(v, tl);
   if constexpr (D == 128) {
-    if (v.tile_waves == 8 && v.col_tiles == 2) return tile_d<D, 8, 2>(v);
+    if (v.tile_waves == 8 && v.col_tiles == 2) return tile_d<D, 8, 2>(v, tl);
   }
   if (v.tile_waves != 0 || v.col_tiles != 1) return nullptr;
-  return v.dup_lo ? kernel_d<D, 1, true>(v) : kernel_d<D, 1, false>(v);
+  return v.dup_lo ? kernel_d<D, 1, true>(v, tl) : kernel_d<D, 1, false>(v, tl);
 }
 
-static const void* stream_kernel(const Variant& v) {
-  if (v.head_dim == 128) return kernel_tiles<128>(v);
-  if (v.head_dim == 64) return kernel_tiles<64>(v);
+static const void* stream_kernel(const Variant& v, bool tl = false) {
+  if (v.head_dim == 128) return kernel_tiles<128>(v, tl);
+  if (v.head_dim == 64) return kernel_tiles<64>(v, tl);
   return nullptr;
 }
 
@@ -1976,10 +2053,12 @@ hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, 64 * waves_per_group(v), 0);
 }
 
+bool timeline_supported(const Variant& v) { return stream_kernel(v, true) != nullptr; }
+
 hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int grid, hipStream_t stream,
                                    hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (grid <= 0) return hipSuccess;
-  const void* f = stream_kernel(v);
+  const void* f = stream_kernel(v, p.timeline != nullptr);
   if (!f) return hipErrorInvalidValue;
   void* args[] = {const_cast<StreamParams*>(&p)};
   if (ev_start) {

@@ -8,6 +8,7 @@
 namespace pa {
 
 constexpr int kPageSize = 16;  // tokens per page
+constexpr int kTimelineSlots = 64;  // event words per wave in a timeline row
 
 // KV formats: OCP E4M3 bytes; INT8 bytes; INT4, two 4-bit two's-complement
 // codes per byte (low nibble first), head_dim 128 only.
@@ -42,6 +43,7 @@ struct StreamParams {
   int32_t max_units;           // units sharing the chunks at most (waves or workgroups)
   int32_t start_cost;          // chunks a segment's start counts for in the balanced split
   int32_t whole_ok;            // the tile kernel may give each unit one segment whole
+  unsigned long long* timeline;  // null, or [waves][64] event words (measurement)
   int64_t v_scale_offset;      // P * Hkv: start of the V scales in kv_scales
   float qk_scale_log2;         // sm_scale * log2(e)
 };
@@ -78,6 +80,7 @@ hipError_t launch_stream_attention(const Variant& v, const StreamParams& p, int 
                                    hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // Resident workgroups per compute unit for the variant's attention kernel.
 hipError_t stream_attention_occupancy(const Variant& v, int* blocks_per_cu);
+bool timeline_supported(const Variant& v);  // kernels that record a timeline exist for v
 // Merge kernel: `grid` = segments workgroups along x, merge_grid_y along y.
 hipError_t launch_split_merge(const Variant& v, const StreamParams& p, int grid, hipStream_t stream,
                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
