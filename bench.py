@@ -509,7 +509,8 @@ def timeline_stats(a: np.ndarray, info: dict) -> dict:
                 cur = None
         gaps = [b - a_ for p_ in pieces for a_, b in zip(p_["steps"], p_["steps"][1:])]
         restarts = [nx["steps"][0] - pv["end"] for pv, nx in zip(pieces, pieces[1:]) if nx["steps"]]
-        units.append({"slot": (r // wpg) // max(1, info["compute_units"]), "first": steps[0] if steps else np.nan,
+        units.append({"slot": (r // wpg) // max(1, info["compute_units"]), "xcd": (r // wpg) % 8,
+                      "first": steps[0] if steps else np.nan,
                       "end": us(tim[r, -1]) if typ[r, -1] == 7 else np.nan, "steps": len(steps),
                       "pieces": len(pieces), "gap": float(np.median(gaps)) if gaps else np.nan,
                       "restarts": restarts, "full": len(ev) >= words - 1})
@@ -539,6 +540,13 @@ def timeline_stats(a: np.ndarray, info: dict) -> dict:
                               "first_step_median_us": pct([x["first"] for x in busy if x["slot"] == sl], 50),
                               "end_median_us": pct([x["end"] for x in busy if x["slot"] == sl], 50)}
                     for sl in slots},
+        # workgroups go to the 8 XCDs in turn: workgroup % 8
+        "by_xcd": {str(xc): {"units": int(sum(x["xcd"] == xc for x in busy)),
+                             "step_interval_median_us": pct([x["gap"] for x in busy
+                                                             if x["xcd"] == xc and np.isfinite(x["gap"])], 50),
+                             "end_median_us": pct([x["end"] for x in busy if x["xcd"] == xc], 50),
+                             "end_max_us": pct([x["end"] for x in busy if x["xcd"] == xc], 100)}
+                   for xc in range(8)},
     }
 
 
@@ -608,6 +616,11 @@ def record_timelines(pt, graph, stream, graph_ms: float, args, n: int = 3) -> di
         lines.append(f"forward0_slot{sl}: units {d['units']} first_step_median_us "
                      f"{fs:.2f} end_median_us {en:.2f}" if fs is not None and en is not None
                      else f"forward0_slot{sl}: units {d['units']}")
+    for xc, d in runs[0]["by_xcd"].items():
+        if d["units"]:
+            lines.append(f"forward0_xcd{xc} (workgroup % 8): units {d['units']} step_interval_median_us "
+                         f"{d['step_interval_median_us'] or float('nan'):.3f} end_median_us {d['end_median_us']:.2f} "
+                         f"end_max_us {d['end_max_us']:.2f}")
     with open(args.timeline_summary, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     return {"medians": medians, "forwards": runs}
