@@ -507,13 +507,22 @@ def timeline_stats(a: np.ndarray, info: dict) -> dict:
                 cur["end"] = t
                 pieces.append(cur)
                 cur = None
+        entry = ev[0][1] if ev and ev[0][0] == 1 else np.nan
+        sched = next((t for k, t in ev if k == 2), np.nan)
+        lens = next((t for k, t in ev if k == 6), np.nan)
+        first_piece = pieces[0] if pieces else None
         gaps = [b - a_ for p_ in pieces for a_, b in zip(p_["steps"], p_["steps"][1:])]
         restarts = [nx["steps"][0] - pv["end"] for pv, nx in zip(pieces, pieces[1:]) if nx["steps"]]
         units.append({"slot": (r // wpg) // max(1, info["compute_units"]), "xcd": (r // wpg) % 8,
                       "first": steps[0] if steps else np.nan,
                       "end": us(tim[r, -1]) if typ[r, -1] == 7 else np.nan, "steps": len(steps),
                       "pieces": len(pieces), "gap": float(np.median(gaps)) if gaps else np.nan,
-                      "restarts": restarts, "full": len(ev) >= words - 1})
+                      "restarts": restarts, "full": len(ev) >= words - 1,
+                      # the start, split: dispatch, schedule, piece set-up, first chunk's data
+                      "entry": entry, "lengths": lens - entry, "sched": sched - lens,
+                      "setup": (first_piece["start"] - sched) if first_piece else np.nan,
+                      "first_data": (first_piece["steps"][0] - first_piece["start"])
+                      if first_piece and first_piece["steps"] else np.nan})
     busy = [x for x in units if x["steps"] > 0]
     f = np.array([x["first"] for x in busy])
     e = np.array([x["end"] for x in busy])
@@ -534,6 +543,8 @@ def timeline_stats(a: np.ndarray, info: dict) -> dict:
         "step_interval_us": {"p10": pct(g, 10), "median": pct(g, 50), "p90": pct(g, 90)},
         "end_us": {"min": pct(e, 0), "median": pct(e, 50), "max": pct(e, 100)},
         "restart_us": {"count": int(len(rs)), "median": pct(rs, 50)},
+        "start_split_us": {k: pct([x[k] for x in busy if np.isfinite(x[k])], 50)
+                           for k in ("entry", "lengths", "sched", "setup", "first_data")},
         "end_corr": {"dispatch_slot": corr("slot"), "first_step": corr("first"), "pieces": corr("pieces"),
                      "steps": corr("steps"), "step_interval": corr("gap")},
         "by_slot": {str(sl): {"units": int(sum(x["slot"] == sl for x in busy)),
@@ -587,6 +598,9 @@ def record_timelines(pt, graph, stream, graph_ms: float, args, n: int = 3) -> di
     keys = [("span_us",), ("first_step_us", "p10"), ("first_step_us", "median"), ("first_step_us", "p90"),
             ("step_interval_us", "p10"), ("step_interval_us", "median"), ("step_interval_us", "p90"),
             ("end_us", "min"), ("end_us", "median"), ("end_us", "max"), ("restart_us", "median"),
+            ("start_split_us", "entry"), ("start_split_us", "lengths"), ("start_split_us", "sched"),
+            ("start_split_us", "setup"),
+            ("start_split_us", "first_data"),
             ("end_corr", "dispatch_slot"), ("end_corr", "first_step"), ("end_corr", "pieces"),
             ("end_corr", "steps"), ("end_corr", "step_interval")]
     medians = {".".join(k): med(k) for k in keys}
@@ -601,10 +615,14 @@ def record_timelines(pt, graph, stream, graph_ms: float, args, n: int = 3) -> di
              f"of the timed steps; times in us from the kernel's first wave start; a unit is a wave (packed "
              f"decode) or a workgroup (its wave 0); dispatch slot = workgroup // compute units; first step = the "
              f"unit's first chunk step; step interval = median gap between consecutive chunk steps of a piece; "
-             f"restart = from a piece's end to the next piece's first step; end_corr = correlation of the "
+             f"restart = from a piece's end to the next piece's first step; start_split = the start's parts: "
+             f"wave start (entry), lengths read and summed (lengths), from there its unit's range known "
+             f"(sched), the first piece's set-up, and from there to the first chunk step (first_data); "
+             f"end_corr = correlation of the "
              f"units' end times with each quantity; the recording runs copies of the kernels with the "
-             f"recording compiled in, whose per-event stores make them a few percent slower than the "
-             f"kernels forwards otherwise run",
+             f"recording compiled in, whose counter reads (each waits for the wave's outstanding LDS "
+             f"and scalar loads) and stores make them slower than the kernels forwards otherwise run "
+             f"(4-22% on the decode, long-context, MTP, MQA and prefill workloads)",
              f"plan: grid {info['grid_size']} waves_per_group {info['waves_per_group']} packed {info['packed']} "
              f"shared_kv {info['shared_kv']} units {runs[0]['units']} with chunks {runs[0]['units_with_chunks']} "
              f"rows full {runs[0]['rows_full']}"]

@@ -210,8 +210,9 @@ attn_status_t attn_plan_set_merge_events(attn_plan_t plan, hipEvent_t merge_star
  * grid_size * waves_per_group (attn_plan_get_info), else
  * ATTN_ERR_INVALID_ARGUMENT.  Word i < ATTN_TIMELINE_WORDS - 1 is the i-th
  * event, (t << 4) | type, t the GPU's constant-rate real-time counter
- * (wallclock_khz ticks per millisecond): type 1 the wave's start, 2 its
- * chunk range known, then per piece of a segment 3 its start, 4 each chunk
+ * (wallclock_khz ticks per millisecond): type 1 the wave's start, 6 the
+ * sequence lengths read and summed, 2 its chunk range known, then per
+ * piece of a segment 3 its start, 4 each chunk
  * step (each group of chunks in the packed decode), 5 its end; events past
  * the row's first ATTN_TIMELINE_WORDS - 1 words are dropped.  The last word
  * is (t << 4) | 7 at the wave's end.  Words nothing writes keep their

@@ -222,19 +222,47 @@ __device__ __forceinline__ int head_chunks(const StreamParams& p, int L, int Q) 
   return s;
 }
 
-__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+// ---- wave-wide scans without LDS -------------------------------------------
+// Within each row of 16 lanes a Hillis-Steele scan by DPP row shifts (lanes
+// shifted in from outside the row read 0), then the totals of the rows
+// before are added from scalar reads of lanes 15, 31 and 47.  (Shuffles
+// through ds_bpermute put a round trip through LDS on every step of the
+// schedule at the kernels' start.)
+template <int CTRL>
+__device__ __forceinline__ int64_t dpp_row_shr64(int64_t x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(uint64_t)x, CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)((uint64_t)x >> 32), CTRL, 0xf, 0xf, true);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t x, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)x, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)((uint64_t)x >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ int64_t wave_incl_scan64(int64_t x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
+  x += dpp_row_shr64<0x111>(x);  // row_shr:1
+  x += dpp_row_shr64<0x112>(x);  // row_shr:2
+  x += dpp_row_shr64<0x114>(x);  // row_shr:4
+  x += dpp_row_shr64<0x118>(x);  // row_shr:8
+  const int64_t r0 = readlane64(x, 15), r1 = readlane64(x, 31), r2 = readlane64(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
+  return readlane64(wave_incl_scan64(x, __lane_id()), 63);
+}
+
+// Maximum of non-negative values over the wave (lanes shifted in read 0).
+__device__ __forceinline__ int wave_max_nonneg(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true));
+  return max(max(__builtin_amdgcn_readlane(x, 15), __builtin_amdgcn_readlane(x, 31)),
+             max(__builtin_amdgcn_readlane(x, 47), __builtin_amdgcn_readlane(x, 63)));
 }
 
 // Lengths of sequence b and its chunk count over all kv heads (zeros for
@@ -285,14 +313,14 @@ __device__ __forceinline__ SeqStart locate_seq(const StreamParams& p, int64_t po
       const int src = __builtin_ctzll(hit);
       SeqStart s;
       s.b = base + src;
-      s.chunk0 = __shfl(start, src);
-      s.row0 = rows + __shfl(qincl - c.Q, src);
-      s.L = __shfl(c.L, src);
-      s.Q = __shfl(c.Q, src);
+      s.chunk0 = readlane64(start, src);
+      s.row0 = rows + __builtin_amdgcn_readlane(qincl - c.Q, src);
+      s.L = __builtin_amdgcn_readlane(c.L, src);
+      s.Q = __builtin_amdgcn_readlane(c.Q, src);
       return s;
     }
-    carry += __shfl(incl, 63);
-    rows += __shfl(qincl, 63);
+    carry += readlane64(incl, 63);
+    rows += __builtin_amdgcn_readlane(qincl, 63);
   }
   SeqStart s{p.num_seqs, carry, rows, 0, 0};  // not reached for pos < total
   return s;
@@ -307,7 +335,7 @@ __device__ __forceinline__ void write_seq_meta(const StreamParams& p, int lane) 
     const int qb = (b < p.num_seqs) ? p.q_lens[b] : 0;
     const int qincl = (int)wave_incl_scan64(qb, lane);
     if (b < p.num_seqs) p.seq_row0[b] = rows + qincl - qb;
-    rows += __shfl(qincl, 63);
+    rows += __builtin_amdgcn_readlane(qincl, 63);
   }
 }
 
@@ -391,14 +419,17 @@ struct PieceDesc {
 // Measurement: the kernels instantiated with ON record, for every wave, events
 // in its own row of kTimelineSlots words of p.timeline (row = workgroup x
 // waves per workgroup + wave), each (s_memrealtime << 4) | type, in order:
-// kTlEntry, kTlScheduled (its unit's range known), then per piece
+// kTlEntry, kTlLengths (the lengths read and summed), kTlScheduled (its
+// unit's range known), then per piece
 // kTlPieceStart, kTlStep per chunk (per group of chunks in the packed
 // decode), kTlPieceEnd; the row's last word holds kTlWaveEnd.  Events past
 // the row's first kTimelineSlots - 1 words are dropped.  Lane 0 writes;
 // the count is the same in every lane.  The kernels without ON (the ones
 // forwards use unless a timeline is set) contain none of it: a run-time
 // check per chunk step measured 1-4% slower.
-enum : unsigned { kTlEntry = 1, kTlScheduled = 2, kTlPieceStart = 3, kTlStep = 4, kTlPieceEnd = 5, kTlWaveEnd = 7 };
+enum : unsigned {
+  kTlEntry = 1, kTlScheduled = 2, kTlPieceStart = 3, kTlStep = 4, kTlPieceEnd = 5, kTlLengths = 6, kTlWaveEnd = 7
+};
 template <bool ON>
 struct Timeline {
   unsigned long long* row;
@@ -1716,9 +1747,9 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
 // segment whole: no partials are written and the merge has nothing to do.
 // The balanced split would cut nearly every segment in two there, and the
 // partial writes and their merge cost more than the longest segment's
-// excess over the mean.  The longest segments go to the lowest unit
-// numbers, which the dispatcher starts first (later workgroups of a compute
-// unit start and step later).  Every unit takes the same decision from the
+// excess over the mean.  The longest segments (by length class) go to the
+// lowest unit numbers, which the dispatcher starts first (later workgroups
+// of a compute unit start and step later).  Every unit takes the same decision from the
 // same lengths.  Needs at most 128 sequences (their lengths sit in the
 // lanes of c0 and c1) and one column block per (sequence, kv head); unit w
 // takes kv head w % Hkv of the sequence ranked w / Hkv.  Returns false for
@@ -1731,23 +1762,34 @@ __device__ __forceinline__ bool whole_segment_piece(const StreamParams& p, int l
   if (S > W || 4 * S < 3 * W) return false;
   const int n0 = seg_chunks(c0.L, c0.Q, p.group, p.cols_per_block, 0);
   const int n1 = seg_chunks(c1.L, c1.Q, p.group, p.cols_per_block, 0);
-  int mx = max(n0, n1);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  const int mx = wave_max_nonneg(max(n0, n1));
   const int64_t sum = wave_sum64((int64_t)n0 + n1);
   if ((int64_t)mx * p.num_seqs > 2 * sum) return false;
   pc.c_end = 0;
   if (w >= S) return true;
-  // rank of each lane's two sequences (lane and 64 + lane) by chunks,
-  // longest first, ties by sequence index
+  // rank of each lane's two sequences (lane and 64 + lane): by class of
+  // chunk count, kWholeClasses classes of equal width up to the longest,
+  // longest class first, by sequence index within a class.  One ballot per
+  // class and bit counts: an exact sort of the 128 counts through lane reads
+  // took ~6 us here, at the start of every unit; with 8, 16 and 32 classes
+  // MTP verification measured 46.6-47.1, 47.3-47.6 and 48.3-48.5 us.
+  constexpr int kWholeClasses = 8;
+  const int cls0 = (n0 * kWholeClasses) / (mx + 1);
+  const int cls1 = (n1 * kWholeClasses) / (mx + 1);
+  const bool real0 = lane < p.num_seqs;
+  const bool real1 = 64 + lane < p.num_seqs;
   int rk0 = 0, rk1 = 0;
-  for (int j = 0; j < 64; ++j) {
-    const int a0 = __builtin_amdgcn_readlane(n0, j);
-    const int a1 = __builtin_amdgcn_readlane(n1, j);
-    rk0 += (a0 > n0 || (a0 == n0 && j < lane)) ? 1 : 0;
-    rk0 += (a1 > n0) ? 1 : 0;
-    rk1 += (a0 >= n1) ? 1 : 0;
-    rk1 += (a1 > n1 || (a1 == n1 && j < lane)) ? 1 : 0;
+  int above = 0;  // sequences in the longer classes
+  for (int c = kWholeClasses - 1; c >= 0; --c) {
+    const uint64_t m0 = __builtin_amdgcn_ballot_w64(real0 && cls0 == c);
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(real1 && cls1 == c);
+    const int k0 = __popcll(m0);
+    // members of the class in lanes below this one
+    const int b0 = __builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, 0));
+    const int b1 = __builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0));
+    if (cls0 == c) rk0 = above + b0;
+    if (cls1 == c) rk1 = above + k0 + b1;
+    above += k0 + __popcll(m1);
   }
   const int r = w / p.num_kv_heads;
   const uint64_t hit0 = __builtin_amdgcn_ballot_w64(rk0 == r && lane < p.num_seqs);
@@ -1760,11 +1802,12 @@ __device__ __forceinline__ bool whole_segment_piece(const StreamParams& p, int l
   pc.b = (in0 ? 0 : 64) + src;
   pc.h = w - r * p.num_kv_heads;
   pc.cb = 0;
-  pc.L = in0 ? __shfl(c0.L, src) : __shfl(c1.L, src);
-  pc.Q = in0 ? __shfl(c0.Q, src) : __shfl(c1.Q, src);
-  pc.row0 = (in0 ? __shfl(q0, src) : __shfl(q0, 63) + __shfl(q1, src)) - pc.Q;
+  pc.L = __builtin_amdgcn_readlane(in0 ? c0.L : c1.L, src);
+  pc.Q = __builtin_amdgcn_readlane(in0 ? c0.Q : c1.Q, src);
+  pc.row0 = (in0 ? __builtin_amdgcn_readlane(q0, src)
+                 : __builtin_amdgcn_readlane(q0, 63) + __builtin_amdgcn_readlane(q1, src)) - pc.Q;
   pc.c_begin = 0;
-  pc.c_end = in0 ? __shfl(n0, src) : __shfl(n1, src);
+  pc.c_end = __builtin_amdgcn_readlane(in0 ? n0 : n1, src);
   pc.whole = true;
   const int seg = pc.b * p.num_kv_heads + pc.h;
   pc.slot = seg + w;
@@ -1799,6 +1842,7 @@ __global__ __launch_bounds__(64 * (NCT == 0 ? kPackedWaves : kWavesPerGroup),
   const SeqLens c1 = load_seq(p, 64 + lane);
   const int64_t T = total_chunks(p, lane, c0, c1);
   const int W = work_units(p, T);
+  tl.rec(kTlLengths, lane);
   tl.rec(kTlScheduled, lane);
   if (w < W) {
     walk_pieces(p, lane, leader, w, W, T, c0, c1, [&](const PieceDesc& pc) {
@@ -1848,6 +1892,7 @@ __global__ __launch_bounds__(64 * NW, (TileCfg<NW, NT>::WAVES_PER_SIMD)) void at
   const SeqLens c1 = load_seq(p, 64 + lane);
   const int64_t T = total_chunks(p, lane, c0, c1);
   const int W = work_units(p, T);
+  tl.rec(kTlLengths, lane);
   if (w < W) {
     PieceDesc whole;
     if (whole_segment_piece(p, lane, leader, w, W, c0, c1, whole)) {

@@ -39,6 +39,10 @@ def test_timeline_stats_tile_units():
     assert st["restart_us"]["count"] == 1 and st["restart_us"]["median"] == 115 - 110
     assert st["end_us"]["min"] == 20.0 and st["end_us"]["max"] == 40.0
     assert [st["by_slot"][k]["units"] for k in ("0", "1", "2")] == [1, 1, 1]
+    # start split, medians over the three units: entries 0, 3, 5; schedule 1, 1, 1;
+    # set-up 1, 0, 1; first data 3, 6, 13
+    assert st["start_split_us"]["entry"] == 3.0 and st["start_split_us"]["setup"] == 1.0
+    assert st["start_split_us"]["first_data"] == 6.0
     assert abs(st["end_corr"]["dispatch_slot"] - 1.0) < 1e-12
 
 

@@ -67,10 +67,10 @@ def test_timeline_rows(case):
         types = [t for t, _ in ev]
         times = [t for _, t in ev] + [int(tim[r, -1])]
         assert all(b >= a_ for a_, b in zip(times, times[1:])), (case, r)
-        assert types[:2] == [1, 2], (case, r, types[:4])
+        assert types[:3] == [1, 6, 2], (case, r, types[:4])
         # pieces: 3, then 4s, then 5, repeated (the row may end early when full)
         state = 5
-        for t in types[2:]:
+        for t in types[3:]:
             if t == 3:
                 assert state == 5
             elif t == 4:
@@ -79,7 +79,7 @@ def test_timeline_rows(case):
                 assert t == 5 and state in (3, 4)
             state = t
         if len(types) < TIMELINE_WORDS - 1:
-            assert state == 5 or len(types) == 2, (case, r)
+            assert state == 5 or len(types) == 3, (case, r)
         if not info["packed"] and r % info["waves_per_group"] == 0:
             steps_first_waves += types.count(4)
     if not info["packed"]:

@@ -115,17 +115,16 @@ def test_empty_start_piece_is_possible_and_covered():
 # before each of its own.
 
 def _kernel_ranks(n):
-    n = list(n) + [0] * (128 - len(n))
-    rk = [0] * 128
-    for lane in range(64):
-        n0, n1 = n[lane], n[64 + lane]
-        r0 = r1 = 0
-        for j in range(64):
-            a0, a1 = n[j], n[64 + j]
-            r0 += (a0 > n0 or (a0 == n0 and j < lane)) + (a1 > n0)
-            r1 += (a0 >= n1) + (a1 > n1 or (a1 == n1 and j < lane))
-        rk[lane], rk[64 + lane] = r0, r1
-    return rk
+    """Ranks as the kernel computes them: 8 classes of equal width of the
+    chunk count up to the longest, the longest class first, sequence index
+    within a class (sequences past len(n) hold 0 chunks and no rank)."""
+    mx = max(n) if n else 0
+    cls = [(x * 8) // (mx + 1) for x in n]
+    order = sorted(range(len(n)), key=lambda i: (-cls[i], i))
+    rk = [0] * len(n)
+    for r, i in enumerate(order):
+        rk[i] = r
+    return rk + [0] * (128 - len(n))
 
 
 def _whole_decision(n, H, W):
@@ -151,14 +150,22 @@ def _whole_units(n, H, W):
     return out
 
 
-def test_kernel_ranks_are_the_stable_descending_order():
+def test_kernel_ranks_order_by_length_class():
     rng = random.Random(11)
     for _ in range(300):
         B = rng.randint(1, 128)
         n = [rng.choice([rng.randint(0, 3), rng.randint(1, 40), 7]) for _ in range(B)]
         rk = _kernel_ranks(n)[:B]
-        order = sorted(range(B), key=lambda i: (-n[i], i))
-        assert [rk[i] for i in order] == list(range(B))
+        assert sorted(rk) == list(range(B))
+        by_rank = [n[i] for i in sorted(range(B), key=lambda i: rk[i])]
+        # a sequence ranked after another is shorter, or in the same class
+        mx = max(n)
+        width = (mx + 1) / 8
+        for a, b in zip(by_rank, by_rank[1:]):
+            assert b <= a or b - a < width
+        # exact order where the classes separate the lengths: all distinct classes
+        if len(set((x * 8) // (mx + 1) for x in n)) == B:
+            assert by_rank == sorted(n, reverse=True)
 
 
 def test_whole_segment_units_cover_each_segment_once():
@@ -177,9 +184,10 @@ def test_whole_segment_units_cover_each_segment_once():
         units = _whole_units(n, H, W)
         got = sorted(u for u in units if u is not None and u[3] > u[2])
         assert got == [(b, h, 0, n[b]) for b in range(B) for h in range(H) if n[b] > 0]
-        # longest first: unit numbers rise as the segments shorten
-        lens = [u[3] for u in units if u is not None]
-        assert lens == sorted(lens, reverse=True)
+        # longest class first: unit numbers rise as the classes shorten
+        mx = max(n)
+        cls = [(u[3] * 8) // (mx + 1) for u in units if u is not None]
+        assert cls == sorted(cls, reverse=True)
     assert seen > 50
 
 
