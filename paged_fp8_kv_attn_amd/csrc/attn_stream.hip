@@ -430,21 +430,28 @@ struct PieceDesc {
 enum : unsigned {
   kTlEntry = 1, kTlScheduled = 2, kTlPieceStart = 3, kTlStep = 4, kTlPieceEnd = 5, kTlLengths = 6, kTlWaveEnd = 7
 };
+// An event's word is stored at the next event (or the wave's end): the
+// counter read then has had a whole step to return, and the wave does not
+// wait for it (and, with it, for its outstanding LDS accesses) where it is
+// taken.
 template <bool ON>
 struct Timeline {
   unsigned long long* row;
   int n;
+  unsigned long long pending;
   __device__ __forceinline__ void rec(unsigned type, int lane) {
     if constexpr (ON) {
       if (n < kTimelineSlots - 1) {
         const unsigned long long t = __builtin_amdgcn_s_memrealtime();
-        if (lane == 0) row[n] = (t << 4) | type;
+        if (n > 0 && lane == 0) row[n - 1] = pending;
+        pending = (t << 4) | type;
         ++n;
       }
     }
   }
   __device__ __forceinline__ void end(int lane) {
     if constexpr (ON) {
+      if (n > 0 && lane == 0) row[n - 1] = pending;
       const unsigned long long t = __builtin_amdgcn_s_memrealtime();
       if (lane == 0) row[kTimelineSlots - 1] = (t << 4) | kTlWaveEnd;
     }
@@ -456,6 +463,7 @@ __device__ __forceinline__ Timeline<ON> timeline_for(const StreamParams& p, int 
   Timeline<ON> tl;
   tl.row = ON ? p.timeline + ((size_t)blockIdx.x * (blockDim.x / 64) + wave) * kTimelineSlots : nullptr;
   tl.n = 0;
+  tl.pending = 0;
   return tl;
 }
 
