@@ -719,6 +719,9 @@ def main():
     ap.add_argument("--kv-format", default="e4m3", choices=["e4m3", "int8", "int4"],
                     help="KV format of the attention workloads (INT8: two's-complement bytes times the page "
                          "scale; INT4: two 4-bit codes per byte, attention workloads of head_dim 128 only)")
+    ap.add_argument("--kv-piece-len", type=int, default=0,
+                    help="attention workloads: plans with this kv_piece_len (batch-invariant fixed pieces of "
+                         "this many keys, a multiple of 32; 0: the balanced split)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--timeline-summary", default=None,
                     help="attention workloads: record per-wave timelines of three more forwards "
@@ -772,8 +775,9 @@ def main():
             self.plan = Plan(num_seqs=w.num_seqs, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                              head_dim=w.head_dim, num_pages=w.num_pages, max_pages_per_seq=w.max_pages_per_seq,
                              max_q_len=w.max_q_len, max_ctx_len=w.max_ctx_len, q_dtype=w.q_dtype,
-                             out_dtype=w.out_dtype, sm_scale=w.sm_scale, num_kv_splits=w.num_kv_splits,
-                             kv_format=w.kv_format)
+                             out_dtype=w.out_dtype, sm_scale=w.sm_scale,
+                             num_kv_splits=0 if args.kv_piece_len else w.num_kv_splits,
+                             kv_format=w.kv_format, kv_piece_len=args.kv_piece_len)
             self.q = w.q.to(dev)
             self.bt = t(w.block_table)
             self.ctx = t(w.ctx_lens)
@@ -979,7 +983,7 @@ def main():
             if ceil is not None:
                 roof["stream_ceiling"] = {"GB/s": ceil["GB/s"], "chunk_bytes": ceil["chunk_bytes"],
                                           "frac": k_gbs / ceil["GB/s"], "source": ceil["source"]}
-        sq = committed_sq_counters(profile_name(pt.w), pt.kernel)
+        sq = None if args.kv_piece_len else committed_sq_counters(profile_name(pt.w), pt.kernel)
         if sq is not None:
             roof["sq_counters"] = sq
         if pt.merge_ms:
@@ -994,7 +998,9 @@ def main():
 
     # the dominant kernel: the attention kernel with the largest share of the step
     dom = max(parts, key=lambda pt: pt.attn_ms)
-    roof = roofline(dom, committed_traffic(profile_name(dom.w), dom.kernel))
+    # the committed counters were taken with the balanced split, not fixed pieces
+    traffic_of = lambda pt: None if args.kv_piece_len else committed_traffic(profile_name(pt.w), pt.kernel)  # noqa: E731
+    roof = roofline(dom, traffic_of(dom))
     if len(parts) > 1:
         roof["workload_part"] = dom.w.name
 
@@ -1010,6 +1016,8 @@ def main():
     else:
         config = {"workload": args.workload, "parts": [workload_config(pt.w) for pt in parts],
                   "order": "back to back on one stream, in the order listed"}
+    if args.kv_piece_len:
+        config["kv_piece_len"] = args.kv_piece_len
     res = {
         "metric": METRIC,
         "value": gbs,
@@ -1040,7 +1048,7 @@ def main():
         "cpu_baseline": None,
     }
     if len(parts) > 1:
-        res["parts"] = [{"workload": pt.w.name, "roofline": roofline(pt, committed_traffic(profile_name(pt.w), pt.kernel))}
+        res["parts"] = [{"workload": pt.w.name, "roofline": roofline(pt, traffic_of(pt))}
                         for pt in parts]
     if args.workload in APPEND_WORKLOADS:
         res["dtype"] = "f32 (correctly rounded divide) -> " + ("int8" if args.kv_format == "int8" else "fp8 e4m3")

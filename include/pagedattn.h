@@ -128,7 +128,21 @@ typedef struct {
                                 partitions (so each of equal-length segments
                                 gets exactly n), merged by log-sum-exp */
   int32_t kv_format;         /* ATTN_KV_E4M3 (0), ATTN_KV_INT8 (1) or ATTN_KV_INT4 (2) */
-  int32_t reserved[3];       /* must be zero */
+  int32_t kv_piece_len;      /* 0: off.  k = 32 times a power of two, with
+                                num_kv_splits 0: batch-invariant split.  The
+                                keys of every segment are cut every k keys
+                                from its first key; each piece is computed on
+                                its own and the pieces of a segment are merged
+                                in an order fixed by their count.  A sequence's
+                                output then depends only on its own q, lengths
+                                and pages, not on the other sequences, num_seqs
+                                or max_ctx_len, among plans with the same
+                                heads, head_dim, max_q_len, dtypes, kv_format
+                                and kv_piece_len (bit-identical rows).  The
+                                workspace holds one partial per piece:
+                                segments * ceil(ceil(max_ctx_len/32) / (k/32))
+                                of them.  Any other value: INVALID_ARGUMENT. */
+  int32_t reserved[2];       /* must be zero */
 } attn_plan_desc_t;
 
 /* What the plan chose (for tests and measurement).  A segment is one

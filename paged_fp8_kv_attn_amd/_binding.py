@@ -69,7 +69,8 @@ class PlanDesc(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("num_kv_splits", ctypes.c_int32),
         ("kv_format", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("kv_piece_len", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -278,7 +279,7 @@ def check_append_tensors(desc: "PlanDesc", device, k_new, v_new, k_pages, v_page
 
 def make_desc(*, num_seqs, num_q_heads, num_kv_heads, head_dim, num_pages, max_pages_per_seq, max_q_len,
               max_ctx_len, q_dtype="bf16", out_dtype="bf16", sm_scale=0.0, num_kv_splits=0, page_size=16,
-              kv_format="e4m3", reserved=(0, 0, 0)) -> PlanDesc:
+              kv_format="e4m3", kv_piece_len=0, reserved=(0, 0)) -> PlanDesc:
     """A filled attn_plan_desc_t."""
     d = PlanDesc()
     d.num_seqs = num_seqs
@@ -295,6 +296,7 @@ def make_desc(*, num_seqs, num_q_heads, num_kv_heads, head_dim, num_pages, max_p
     d.sm_scale = float(sm_scale)
     d.num_kv_splits = num_kv_splits
     d.kv_format = KV_FORMATS.get(kv_format, kv_format) if isinstance(kv_format, str) else kv_format
+    d.kv_piece_len = kv_piece_len
     for i, r in enumerate(reserved):
         d.reserved[i] = r
     return d
@@ -322,12 +324,13 @@ class Plan:
 
     def __init__(self, *, num_seqs, num_q_heads, num_kv_heads, head_dim, num_pages, max_pages_per_seq,
                  max_q_len, max_ctx_len, q_dtype="bf16", out_dtype="bf16", sm_scale=0.0, num_kv_splits=0,
-                 page_size=16, kv_format="e4m3", reserved=(0, 0, 0)):
+                 page_size=16, kv_format="e4m3", kv_piece_len=0, reserved=(0, 0)):
         lib = load_library()
         d = make_desc(num_seqs=num_seqs, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
                       num_pages=num_pages, max_pages_per_seq=max_pages_per_seq, max_q_len=max_q_len,
                       max_ctx_len=max_ctx_len, q_dtype=q_dtype, out_dtype=out_dtype, sm_scale=sm_scale,
-                      num_kv_splits=num_kv_splits, page_size=page_size, kv_format=kv_format, reserved=reserved)
+                      num_kv_splits=num_kv_splits, page_size=page_size, kv_format=kv_format,
+                      kv_piece_len=kv_piece_len, reserved=reserved)
         self.desc = d
         self._h = ctypes.c_void_p()
         _check(lib.attn_plan_create(ctypes.byref(d), ctypes.byref(self._h)), "attn_plan_create")

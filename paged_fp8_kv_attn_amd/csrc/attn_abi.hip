@@ -34,6 +34,8 @@ struct attn_plan_s {
   int unit_min_chunks;  // chunks per unit at least (within [1, max_units] units)
   int start_cost;       // chunks a segment's start counts for in the balanced split
   bool whole_ok;        // the tile kernel may give each unit one segment whole
+  int piece_chunks;     // > 0: every segment cut into fixed pieces of this many chunks
+  int piece_log2;       // log2(piece_chunks), a power of two
   uint64_t* timeline;   // null, or the caller's timeline rows
   int wallclock_khz;    // rate of the timeline's counter
   int occupancy;     // resident attention workgroups per compute unit
@@ -97,6 +99,10 @@ attn_status_t validate_desc(const attn_plan_desc_t& d) {
   if (d.out_dtype != ATTN_DTYPE_F32 && d.out_dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARGUMENT;
   if (!(d.sm_scale >= 0.f) || !std::isfinite(d.sm_scale)) return ATTN_ERR_INVALID_ARGUMENT;
   if (d.num_kv_splits < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (d.kv_piece_len < 0 || d.kv_piece_len % kChunkTokens != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  const int piece_chunks = d.kv_piece_len / kChunkTokens;
+  if ((piece_chunks & (piece_chunks - 1)) != 0) return ATTN_ERR_INVALID_ARGUMENT;  // a power of two
+  if (d.kv_piece_len > 0 && d.num_kv_splits > 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (d.kv_format != ATTN_KV_E4M3 && d.kv_format != ATTN_KV_INT8 && d.kv_format != ATTN_KV_INT4)
     return ATTN_ERR_INVALID_ARGUMENT;
   if (d.kv_format != ATTN_KV_E4M3 && (d.q_dtype != ATTN_DTYPE_BF16 || d.out_dtype != ATTN_DTYPE_BF16))
@@ -199,7 +205,15 @@ attn_status_t choose_plan(const attn_plan_desc_t& d, int device, attn_plan_s* p)
   // the GPU keeps resident at once, so that every unit streams an equal
   // share in a single round; the kernel uses one per unit_min_chunks chunks
   // of the actual lengths, at most that many.
-  const int64_t max_chunks = segments * ceil_div(d.max_ctx_len, kChunkTokens);
+  const int64_t seg_max_chunks = ceil_div(d.max_ctx_len, kChunkTokens);
+  const int64_t max_chunks = segments * seg_max_chunks;
+  // Fixed pieces: the positions the units share are pieces, at most
+  // ceil(chunks / piece) per segment.
+  p->piece_chunks = d.kv_piece_len / kChunkTokens;
+  p->piece_log2 = 0;
+  while ((1 << p->piece_log2) < p->piece_chunks) ++p->piece_log2;
+  const int64_t seg_max_pieces = p->piece_chunks > 0 ? ceil_div(seg_max_chunks, p->piece_chunks) : 0;
+  const int64_t max_positions = p->piece_chunks > 0 ? segments * seg_max_pieces : max_chunks;
   const int64_t wpg = pa::waves_per_group(v);
   const int64_t unit_waves = v.packed ? 1 : wpg;
   int64_t units;
@@ -209,9 +223,12 @@ attn_status_t choose_plan(const attn_plan_desc_t& d, int device, attn_plan_s* p)
     p->unit_min_chunks = 1;
   } else {
     units = static_cast<int64_t>(p->num_cus) * p->occupancy * wpg / unit_waves;
-    p->unit_min_chunks = v.packed ? kMinChunksPerWave : v.tile_waves > 0 ? kMinChunksPerTile : kMinChunksPerGroup;
+    p->unit_min_chunks = p->piece_chunks > 0 ? 1
+                         : v.packed          ? kMinChunksPerWave
+                         : v.tile_waves > 0  ? kMinChunksPerTile
+                                             : kMinChunksPerGroup;
   }
-  units = std::min<int64_t>(units, std::max<int64_t>(1, max_chunks / p->unit_min_chunks));
+  units = std::min<int64_t>(units, std::max<int64_t>(1, max_positions / p->unit_min_chunks));
   units = std::max<int64_t>(units, 1);
   if (units > 0x3fffffffLL) return ATTN_ERR_UNSUPPORTED;
   p->max_units = static_cast<int>(units);
@@ -225,29 +242,38 @@ attn_status_t choose_plan(const attn_plan_desc_t& d, int device, attn_plan_s* p)
   // whose restart also refills the ring and LDS staging (the prefill chunk
   // 420 us with 3 or 4 against 432 us with 2; MQA and MTP unchanged).  A
   // forced split count keeps its exact cut: n equal pieces of every segment.
-  p->start_cost = d.num_kv_splits != 0 ? 0 : (v.packed ? kStartCostPacked : kStartCostTile);
+  p->start_cost = d.num_kv_splits != 0 || p->piece_chunks > 0 ? 0 : (v.packed ? kStartCostPacked : kStartCostTile);
   // Where the segments are about as many as the units and of similar
   // lengths, the shared-KV tile kernel gives each unit one segment whole
   // (it decides from the lengths of each forward): the MTP verification
   // shape (1024 segments of 4-36 chunks) then ran 54.9-55.3 us per step
   // against 58.8-59.0 us for the balanced split (kernel 50.3-50.4 against
   // 48.6-49.0 us; the merge finds nothing to do).  Not with a forced split
-  // count.
-  p->whole_ok = d.num_kv_splits == 0 && v.tile_waves > 0;
+  // count or fixed pieces.
+  p->whole_ok = d.num_kv_splits == 0 && p->piece_chunks == 0 && v.tile_waves > 0;
   p->timeline = nullptr;
   p->wallclock_khz = 0;
   if (hipDeviceGetAttribute(&p->wallclock_khz, hipDeviceAttributeWallClockRate, device) != hipSuccess)
     p->wallclock_khz = 0;
   p->grid = static_cast<int>(ceil_div(units * unit_waves, wpg));
   // merge: one workgroup per segment (and slice of its columns); segments
-  // with many pieces on average get fewer columns per workgroup
-  p->merge_grid = units > 1 ? p->num_segments : 0;
-  p->merge_cols = pa::merge_cols_for(v, p->cols_per_block, (units + segments - 1) / segments);
+  // with many pieces on average get fewer columns per workgroup.  Fixed
+  // pieces take the widest slices whatever the batch, so that the order in
+  // which a segment's pieces are combined depends on their count alone.
+  if (p->piece_chunks > 0) {
+    p->merge_grid = seg_max_pieces > 1 ? p->num_segments : 0;
+    p->merge_cols = pa::merge_cols_for(v, p->cols_per_block, 1);
+  } else {
+    p->merge_grid = units > 1 ? p->num_segments : 0;
+    p->merge_cols = pa::merge_cols_for(v, p->cols_per_block, (units + segments - 1) / segments);
+  }
 
   // Workspace: partial slots (segments + units of them, one per (segment,
-  // unit) pair that can occur), each sequence's first query row, and each
-  // segment's partial slots.
-  const size_t slots = static_cast<size_t>(segments) + static_cast<size_t>(units);
+  // unit) pair that can occur; with fixed pieces one per piece), each
+  // sequence's first query row, and each segment's partial slots.
+  const size_t slots = p->piece_chunks > 0 ? static_cast<size_t>(max_positions)
+                                           : static_cast<size_t>(segments) + static_cast<size_t>(units);
+  if (slots > 0x3fffffffULL) return ATTN_ERR_UNSUPPORTED;
   p->ws_o_bytes = round_up256(slots * p->cols_per_block * d.head_dim * sizeof(float));
   p->ws_ml_bytes = round_up256(slots * p->cols_per_block * 2 * sizeof(float));
   p->ws_r0_bytes = round_up256(static_cast<size_t>(d.num_seqs) * sizeof(int32_t));
@@ -311,6 +337,8 @@ attn_status_t enqueue_forward(const attn_plan_s* plan, const void* q, const uint
   sp.max_units = plan->max_units;
   sp.start_cost = plan->start_cost;
   sp.whole_ok = plan->whole_ok ? 1 : 0;
+  sp.piece_chunks = plan->piece_chunks;
+  sp.piece_log2 = plan->piece_log2;
   sp.timeline = reinterpret_cast<unsigned long long*>(plan->timeline);
   sp.seq_row0 = plan->seq_row0;
   sp.seg_merge = plan->seg_merge;

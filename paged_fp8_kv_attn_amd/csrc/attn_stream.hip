@@ -208,8 +208,11 @@ __device__ __forceinline__ int seg_chunks(int L, int Q, int G, int cpb, int cb) 
 // What a segment counts for in the balanced split: its chunks, plus
 // p.start_cost for its start, and nothing without chunks.  Position v of a
 // segment's count is its chunk v - start_cost (none for v < start_cost).
+// With fixed pieces (p.piece_chunks = C > 0, a power of two) a segment
+// counts its pieces, position v being its chunks [vC, min((v+1)C, chunks)).
 __device__ __forceinline__ int sched_chunks(const StreamParams& p, int L, int Q, int cb) {
   const int n = seg_chunks(L, Q, p.group, p.cols_per_block, cb);
+  if (p.piece_chunks > 0) return (n + p.piece_chunks - 1) >> p.piece_log2;
   return n > 0 ? n + p.start_cost : 0;
 }
 
@@ -1671,7 +1674,10 @@ __device__ __forceinline__ void run_piece_tile(const StreamParams& p, const Piec
 // runs run(piece) for the part of each segment inside that range, in order.
 // `leader` is the one lane of the unit that records, for each segment whose
 // first chunk lies in its range, where the segment's partials start and how
-// many units hold pieces of it (1: written whole).
+// many units hold pieces of it (1: written whole).  With fixed pieces the
+// positions are pieces: each is run on its own, into the partial slot of
+// its global position, so that where a segment is cut, and every value
+// computed for it, depends on that segment alone.
 template <class Run>
 __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, bool leader, int w, int W, int64_t T,
                                             const SeqLens& c0, const SeqLens& c1, Run&& run) {
@@ -1695,8 +1701,9 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
     n = sched_chunks(p, L, Q, cb);
   }
   int64_t cur = lo;
+  const int C = p.piece_chunks;
   while (true) {
-    const int take = (int)min((int64_t)(n - r), hi - cur);
+    const int take = C > 0 ? 1 : (int)min((int64_t)(n - r), hi - cur);
     PieceDesc pc;
     pc.b = b;
     pc.h = h;
@@ -1707,11 +1714,18 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
     // positions [r, r + take) of the segment's count: its chunks from
     // r - start_cost (a piece holding only the start position has none and
     // writes an empty partial: max -inf, sum 0)
-    pc.c_begin = max(r - p.start_cost, 0);
-    pc.c_end = max(r + take - p.start_cost, 0);
-    pc.whole = (r == 0) && (take == n);
     const int seg = (b * p.num_kv_heads + h) * p.col_blocks + cb;
-    pc.slot = seg + w;
+    if (C > 0) {
+      pc.c_begin = r * C;
+      pc.c_end = min(r * C + C, seg_chunks(L, Q, p.group, p.cols_per_block, cb));
+      pc.whole = n == 1;
+      pc.slot = (int)cur;
+    } else {
+      pc.c_begin = max(r - p.start_cost, 0);
+      pc.c_end = max(r + take - p.start_cost, 0);
+      pc.whole = (r == 0) && (take == n);
+      pc.slot = seg + w;
+    }
     // the same in every lane: hand the piece over in scalar registers
     pc.b = __builtin_amdgcn_readfirstlane(pc.b);
     pc.h = __builtin_amdgcn_readfirstlane(pc.h);
@@ -1724,13 +1738,20 @@ __device__ __forceinline__ void walk_pieces(const StreamParams& p, int lane, boo
     pc.whole = __builtin_amdgcn_readfirstlane((int)pc.whole) != 0;
     pc.slot = __builtin_amdgcn_readfirstlane(pc.slot);
     if (r == 0 && leader) {
-      // units w .. last hold the pieces; their partial slots are seg + w ..
-      const int last = pc.whole ? w : wg_of_chunk(cur + n - 1, T, W);
-      p.seg_merge[seg] = make_int2(seg + w, last - w + 1);
+      if (C > 0) {
+        // its n pieces are at the global positions cur .. cur + n - 1
+        p.seg_merge[seg] = make_int2((int)cur, n);
+      } else {
+        // units w .. last hold the pieces; their partial slots are seg + w ..
+        const int last = pc.whole ? w : wg_of_chunk(cur + n - 1, T, W);
+        p.seg_merge[seg] = make_int2(seg + w, last - w + 1);
+      }
     }
     run(pc);
     cur += take;
     if (cur >= hi) break;
+    r += take;
+    if (r < n) continue;  // fixed pieces: the segment's next piece
     // next non-empty segment
     r = 0;
     do {

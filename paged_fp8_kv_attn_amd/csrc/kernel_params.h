@@ -43,6 +43,8 @@ struct StreamParams {
   int32_t max_units;           // units sharing the chunks at most (waves or workgroups)
   int32_t start_cost;          // chunks a segment's start counts for in the balanced split
   int32_t whole_ok;            // the tile kernel may give each unit one segment whole
+  int32_t piece_chunks;        // > 0: fixed pieces of this many chunks (a power of two); counts are pieces
+  int32_t piece_log2;          // log2(piece_chunks)
   unsigned long long* timeline;  // null, or [waves][64] event words (measurement)
   int64_t v_scale_offset;      // P * Hkv: start of the V scales in kv_scales
   float qk_scale_log2;         // sm_scale * log2(e)

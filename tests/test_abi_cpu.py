@@ -53,7 +53,11 @@ GOOD = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, num_pages=1
     (dict(sm_scale=float("nan")), 1),
     (dict(sm_scale=-1.0), 1),
     (dict(q_dtype=7), 1),
-    (dict(reserved=(0, 1, 0)), 1),
+    (dict(reserved=(0, 1)), 1),
+    (dict(kv_piece_len=-32), 1),
+    (dict(kv_piece_len=48), 1),
+    (dict(kv_piece_len=96), 1),
+    (dict(kv_piece_len=512, num_kv_splits=2), 1),
     (dict(kv_format=3), 1),
     (dict(kv_format="int4", head_dim=64), 2),
     (dict(kv_format="int4", q_dtype="f32"), 2),

@@ -106,6 +106,87 @@ def test_empty_start_piece_is_possible_and_covered():
     assert found
 
 
+# ---- fixed pieces (kv_piece_len > 0) -----------------------------------------
+# A segment of n chunks counts ceil(n / C) positions, position k being its
+# chunks [kC, min((k+1)C, n)); unit w of W = min(units, positions) runs each
+# position in [floor(wT/W), floor((w+1)T/W)) on its own, into the partial
+# slot of its global position, and the unit holding a segment's position 0
+# records (that slot, the segment's piece count).
+
+def _walk_fixed(real, w_max, C):
+    cnt = [-(-n // C) for n in real]
+    T = sum(cnt)
+    W = max(1, min(w_max, T))
+    starts = [0] + list(itertools.accumulate(cnt))
+    pieces = {s: [] for s in range(len(real))}
+    merge = {}
+    for w in range(W):
+        lo, hi = w * T // W, (w + 1) * T // W
+        if lo >= hi:
+            continue
+        s = next(i for i in range(len(real)) if cnt[i] > 0 and starts[i] <= lo < starts[i] + cnt[i])
+        r, cur = lo - starts[s], lo
+        while True:
+            n = cnt[s]
+            pieces[s].append((w, r * C, min(r * C + C, real[s]), n == 1, cur))
+            if r == 0:
+                merge[s] = (cur, n)
+            cur += 1
+            if cur >= hi:
+                break
+            r += 1
+            if r < n:
+                continue
+            r = 0
+            s += 1
+            while cnt[s] == 0:
+                s += 1
+    return pieces, merge
+
+
+def _check_fixed(real, w_max, C):
+    if sum(real) == 0:
+        return
+    pieces, merge = _walk_fixed(real, w_max, C)
+    slot_bound = len(real) * -(-max(real) // C)  # the plan's slots for this many segments
+    slots = set()
+    for s, n in enumerate(real):
+        ps = pieces[s]
+        if n == 0:
+            assert not ps and s not in merge
+            continue
+        # cut points of the segment alone, whatever the other segments and W
+        assert [(cb, ce) for _, cb, ce, _, _ in ps] == [(k * C, min(k * C + C, n)) for k in range(-(-n // C))]
+        for *_, slot in ps:
+            assert 0 <= slot < slot_bound and slot not in slots
+            slots.add(slot)
+        first, count = merge[s]
+        assert count == len(ps) and [p[4] for p in ps] == list(range(first, first + count))
+        assert all(p[3] == (count == 1) for p in ps)
+
+
+@pytest.mark.parametrize("C", [1, 2, 16, 64])
+def test_fixed_pieces_random_mixes(C):
+    rng = random.Random(300 + C)
+    for _ in range(400):
+        real = [rng.choice([0, rng.randint(1, 3), rng.randint(1, 300)]) for _ in range(rng.randint(1, 40))]
+        _check_fixed(real, rng.choice([1, 2, 7, 64, 1024]), C)
+
+
+def test_fixed_pieces_do_not_depend_on_batch_mates():
+    # the same segment among different batch-mates and unit counts is cut
+    # at the same chunks and merged from the same number of pieces
+    rng = random.Random(11)
+    target = 157
+    for _ in range(200):
+        mates = [rng.randint(0, 400) for _ in range(rng.randint(0, 30))]
+        at = rng.randint(0, len(mates))
+        real = mates[:at] + [target] + mates[at:]
+        pieces, merge = _walk_fixed(real, rng.choice([1, 5, 256, 2048]), 16)
+        assert [(cb, ce) for _, cb, ce, _, _ in pieces[at]] == [(k * 16, min(k * 16 + 16, target)) for k in range(10)]
+        assert merge[at][1] == 10
+
+
 # ---- whole-segment schedule of the shared-KV tile kernel --------------------
 # When the segments (one column block each) are at least 3/4 of the units W
 # and at most W, and the longest holds at most twice the mean chunks, unit w
