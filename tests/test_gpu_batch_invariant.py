@@ -40,6 +40,9 @@ PARITY = {
                     512, "int8"),
     "mtp_int4": (lambda: make_workload("mtp_verify", batch=6, ctx_range=(128, 900), kv_format="int4"), 256,
                  "int4"),
+    # full size: 32 sequences x 8 kv heads of up to 8192 keys, 1024-key pieces
+    "decode_full": (lambda: make_workload("llama3_8b_decode", keep_logical=False), 1024, "e4m3"),
+    "mqa_full": (lambda: make_workload("mqa_decode", keep_logical=False), 2048, "e4m3"),
 }
 
 
@@ -98,3 +101,19 @@ def test_rows_do_not_depend_on_the_batch(case):
     check_contract(got_a, _oracle(a, fmt), a.out_dtype, what=f"invariance A {case}")
     check_contract(got_b, _oracle(b, fmt), b.out_dtype, what=f"invariance B {case}")
     assert np.array_equal(got_a[_rows(a, 1)], got_b[_rows(b, 3)]), case
+
+
+def test_full_size_decode_rows_in_another_batch():
+    # a sequence of the 32-sequence decode batch (up to 8192 keys), moved into
+    # a batch of three with other lengths, keeps its rows bit for bit
+    a = make_workload("llama3_8b_decode", keep_logical=False)
+    j = int(np.argmax(a.ctx_lens))
+    b = custom_workload([1] * 4, [100, 3000, 7, int(a.ctx_lens[j])], num_q_heads=a.num_q_heads,
+                        num_kv_heads=a.num_kv_heads, head_dim=a.head_dim, seed=412, keep_logical=False,
+                        name="inv_full_b")
+    _transplant(a, j, b, 3)
+    log(f"batch invariance, full size: sequence {j} of {a.num_seqs} (ctx {int(a.ctx_lens[j])}) piece=1024")
+    got_a, _ = _run(a, 1024, "e4m3")
+    got_b, _ = _run(b, 1024, "e4m3")
+    check_contract(got_b, _oracle(b, "e4m3"), b.out_dtype, what="invariance, full size B")
+    assert np.array_equal(got_a[_rows(a, j)], got_b[_rows(b, 3)])
