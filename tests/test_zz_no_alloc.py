@@ -19,21 +19,21 @@ from tests.gpu_helpers import check_contract, device_inputs, log, out_tensor, pl
 pytestmark = pytest.mark.gpu
 
 
-def _desc(w):
+def _desc(w, **over):
     return make_desc(num_seqs=w.num_seqs, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                      head_dim=w.head_dim, num_pages=w.num_pages, max_pages_per_seq=w.max_pages_per_seq,
                      max_q_len=w.max_q_len, max_ctx_len=w.max_ctx_len, q_dtype=w.q_dtype, out_dtype=w.out_dtype,
-                     sm_scale=w.sm_scale, num_kv_splits=w.num_kv_splits)
+                     sm_scale=w.sm_scale, num_kv_splits=w.num_kv_splits, **over)
 
 
-def _both(w):
+def _both(w, **over):
     """The static forward's output and the plan forward's output."""
     x = device_inputs(w)
     args = (x["q"], x["k_pages"], x["v_pages"], x["kv_scales"], x["block_table"], x["ctx_lens"], x["q_lens"])
     out_s = out_tensor(w)
-    forward_static(_desc(w), *args, out_s)
+    forward_static(_desc(w, **over), *args, out_s)
     torch.cuda.synchronize()
-    plan = plan_for(w)
+    plan = plan_for(w, **over)
     info = plan.info()
     out_p = out_tensor(w)
     plan.forward(*args, out_p)
@@ -53,6 +53,9 @@ CASES = {
             dict(name="mqa_decode", batch=3, ctx_range=(256, 1024))),
     "split": (dict(name="long_ctx_split", batch=2, ctx_range=(0, 4096)),
               dict(name="long_ctx_split", batch=1, ctx_range=(0, 2048))),
+    # fixed pieces of 256 keys (batch-invariant split)
+    "pieces": (dict(name="mqa_decode", batch=8, ctx_range=(256, 4096), kv_piece_len=256),
+               dict(name="llama3_8b_decode", batch=5, ctx_range=(300, 900), kv_piece_len=256)),
 }
 
 
@@ -60,9 +63,10 @@ CASES = {
 def test_static_forward_matches_plan_forward(case):
     for i, spec in enumerate(CASES[case]):
         spec = dict(spec)
+        over = {"kv_piece_len": spec.pop("kv_piece_len")} if "kv_piece_len" in spec else {}
         w = make_workload(spec.pop("name"), **spec)
-        log(f"no-alloc: {case} call {i} B={w.num_seqs} ctx={int(w.ctx_lens.min())}..{int(w.ctx_lens.max())}")
-        got_s, got_p, info = _both(w)
+        log(f"no-alloc: {case} call {i} B={w.num_seqs} ctx={int(w.ctx_lens.min())}..{int(w.ctx_lens.max())} {over}")
+        got_s, got_p, info = _both(w, **over)
         assert info["workspace_bytes"] <= static_scratch_bytes()
         assert info["merge_grid_size"] > 0, "the case should split keys (and use the scratch partials)"
         assert np.array_equal(got_s, got_p, equal_nan=True), f"{case} call {i}: static forward differs"
