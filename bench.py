@@ -621,7 +621,7 @@ def record_timelines(pt, graph, stream, graph_ms: float, args, n: int = 3) -> di
              f"end_corr = correlation of the "
              f"units' end times with each quantity; the recording runs copies of the kernels with the "
              f"recording compiled in, whose counter reads and stores (an event's word is stored at the "
-             f"next event) make them slower than the kernels forwards otherwise run (1-21% on the "
+             f"next event) make them slower than the kernels forwards otherwise run (up to 19% on the "
              f"decode, long-context, MTP, MQA and prefill workloads)",
              f"plan: grid {info['grid_size']} waves_per_group {info['waves_per_group']} packed {info['packed']} "
              f"shared_kv {info['shared_kv']} units {runs[0]['units']} with chunks {runs[0]['units_with_chunks']} "

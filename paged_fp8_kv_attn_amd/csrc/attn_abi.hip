@@ -249,8 +249,9 @@ attn_status_t choose_plan(const attn_plan_desc_t& d, int device, attn_plan_s* p)
   // shape (1024 segments of 4-36 chunks) then ran 54.9-55.3 us per step
   // against 58.8-59.0 us for the balanced split (kernel 50.3-50.4 against
   // 48.6-49.0 us; the merge finds nothing to do).  Not with a forced split
-  // count or fixed pieces.
-  p->whole_ok = d.num_kv_splits == 0 && p->piece_chunks == 0 && v.tile_waves > 0;
+  // count; with fixed pieces only where every segment is one piece (the
+  // kernel checks).
+  p->whole_ok = d.num_kv_splits == 0 && v.tile_waves > 0;
   p->timeline = nullptr;
   p->wallclock_khz = 0;
   if (hipDeviceGetAttribute(&p->wallclock_khz, hipDeviceAttributeWallClockRate, device) != hipSuccess)

@@ -1794,6 +1794,9 @@ __device__ __forceinline__ bool whole_segment_piece(const StreamParams& p, int l
   const int mx = wave_max_nonneg(max(n0, n1));
   const int64_t sum = wave_sum64((int64_t)n0 + n1);
   if ((int64_t)mx * p.num_seqs > 2 * sum) return false;
+  // fixed pieces: only where every segment is one piece, which is then the
+  // piece the walk would run, so only the order of the units changes
+  if (p.piece_chunks > 0 && mx > p.piece_chunks) return false;
   pc.c_end = 0;
   if (w >= S) return true;
   // rank of each lane's two sequences (lane and 64 + lane): by class of

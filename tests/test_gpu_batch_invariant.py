@@ -80,6 +80,9 @@ INVARIANT = {
     "packed_decode": (32, 8, 128, 1, [900, 1234, 40, 3000], [70, 5000, 2, 1234, 800, 16, 4096], 256, "e4m3"),
     "tile_mqa": (64, 1, 128, 1, [2000, 3333, 300], [5000, 16, 700, 3333, 90, 1200, 64, 4100, 2], 512, "e4m3"),
     "tile_mtp": (40, 8, 128, 5, [300, 701, 50], [900, 20, 400, 701] + [333] * 60, 128, "e4m3"),
+    # A: every segment one piece, so the units take whole segments longest
+    # first; B: a longer sequence, so the units walk the pieces
+    "tile_mtp_whole": (40, 8, 128, 5, [300, 701, 400], [900, 20, 5000, 701], 1024, "e4m3"),
     "prefill": (32, 8, 128, 96, [200, 480], [600, 96, 300, 480, 150], 256, "e4m3"),
     "packed_decode_int8": (32, 8, 128, 1, [900, 1234, 40], [5000, 2, 66, 1234, 700], 512, "int8"),
 }
